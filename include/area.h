@@ -1,0 +1,240 @@
+/*
+ * area.h -- C ABI of the adaptive receptive-field attention (AReA) library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * AReA replaces uniform full self-attention of a diffusion transformer above
+ * its native resolution with a receptive field that narrows over the
+ * denoising steps ("AReA: Adaptive Receptive-Field Attention for Efficient
+ * High-Resolution Diffusion Transformers", ai.info summary, section
+ * "Methodology in Plain English"; AReA README introduction):
+ *   Phase I  -- full-resolution queries attend to keys/values pooled one
+ *               token per f x f block onto a near-native grid
+ *               (area_pool_kv + area_coarse_attn);
+ *   Phase II -- queries attend inside shrinking windows, split over smooth
+ *               regions of a Haar detail map, widened by a Halo and joined
+ *               by a global-KV bridge, with centre-weighted blending of
+ *               overlaps (area_dwt_detail + area_window_plan +
+ *               area_window_attn).
+ * area_full_attn is uniform full attention at the same shape, the
+ * baseline the method's speedup is quoted against.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  * Tensors are caller-owned, contiguous DEVICE buffers.  Q, K, V and the
+ *    outputs are bfloat16 laid out [B][H][Gh*Gw][D]; image token n sits at
+ *    grid row y = n / Gw, column x = n % Gw.  Q and K are passed WITHOUT
+ *    rotary embedding: the library rotates them itself (two-axis RoPE: the
+ *    first D/2 channels encode y, the last D/2 encode x, channel pair
+ *    (2k, 2k+1) of an axis half turns by pos * theta^(-4k/D)).
+ *  * The attention MFMAs take IEEE fp16 operands (rotated Q and K, V and
+ *    the probabilities P; three mantissa bits finer than bf16, same rate)
+ *    with fp32 accumulation; the library converts into workspace.  Entries
+ *    of q, k and v must therefore stay below 32768 in magnitude.
+ *  * The library never allocates device memory.  Calls that need scratch
+ *    take a caller-provided workspace of at least area_workspace_bytes()
+ *    bytes (device memory, 256-byte aligned).
+ *  * Every device call validates its arguments on the host first; on any
+ *    error it returns a negative status and launches nothing.  On success
+ *    it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns without synchronising.  A failed launch returns
+ *    AREA_E_HIP.  area_last_error() gives a per-thread description of the
+ *    last failure.
+ *  * Calls are re-entrant: no global mutable state other than the
+ *    thread-local error text.  Two calls that share an output or workspace
+ *    buffer must be ordered by the caller (same stream or events).
+ */
+#ifndef AREA_H
+#define AREA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define AREA_OK             0
+#define AREA_E_INVALID     -1  /* null pointer, bad enum, negative size          */
+#define AREA_E_SHAPE       -2  /* grid / factor / window / bridge inconsistency  */
+#define AREA_E_UNSUPPORTED -3  /* valid request outside what is implemented      */
+#define AREA_E_WORKSPACE   -4  /* workspace missing or too small                 */
+#define AREA_E_HIP         -5  /* a HIP runtime call or kernel launch failed     */
+
+/* ---- enums ------------------------------------------------------------- */
+#define AREA_POOL_MEAN   0     /* average of the f x f block                    */
+#define AREA_POOL_CENTER 1     /* token at offset (f/2, f/2) of the block       */
+
+#define AREA_PHASE_FULL   0    /* canvas at or below native: keep full attention */
+#define AREA_PHASE_COARSE 1    /* Phase I step                                   */
+#define AREA_PHASE_WINDOW 2    /* Phase II step                                  */
+
+#define AREA_OP_FULL   0       /* workspace selectors for area_workspace_bytes */
+#define AREA_OP_COARSE 1
+#define AREA_OP_PLAN   2
+#define AREA_OP_WINDOW 3
+
+/* Plan buffer layout (int32): AREA_PLAN_HEADER header words, then up to
+ * max_windows records of AREA_PLAN_REC words each. */
+#define AREA_PLAN_HEADER 16
+#define AREA_PLAN_REC    10
+/* header word indices */
+#define AREA_PH_NWIN   0       /* windows after quadrant splits                 */
+#define AREA_PH_STEP   1       /* Phase II step index                           */
+#define AREA_PH_W      2       /* scheduled window side                         */
+#define AREA_PH_NY     3       /* base windows along y                          */
+#define AREA_PH_NX     4       /* base windows along x                          */
+#define AREA_PH_JITY   5       /* boundary shift applied along y                */
+#define AREA_PH_JITX   6       /* boundary shift applied along x                */
+#define AREA_PH_HALO   7       /* Halo width                                    */
+#define AREA_PH_R      8       /* bridge tokens per (batch, head); 0 = none     */
+#define AREA_PH_NSPLIT 9       /* base windows that were split                  */
+#define AREA_PH_QTOT  10       /* sum of query-rect areas over all windows      */
+/* record fields: qy0 qx0 qh qw  ky0 kx0 kh kw  parent quadrant(-1 | 0..3) */
+
+/* ---- problem description ------------------------------------------------ */
+typedef struct area_problem {
+  int32_t B, H, D;            /* batch, heads, head dim (64 or 128)              */
+  int32_t Gh, Gw;             /* image token grid (rows, columns)                */
+  int32_t native_h, native_w; /* the model's native token grid                   */
+  int32_t T;                  /* text tokens joined to every key set (must be 0) */
+  float   rope_theta;         /* RoPE base, e.g. 10000                           */
+  int32_t p1_steps;           /* Phase I (coarse) steps                          */
+  int32_t f0;                 /* first pooling factor; 0 = derive from native    */
+  int32_t f_min;              /* pooling floor (2)                               */
+  int32_t pool_mode;          /* AREA_POOL_MEAN | AREA_POOL_CENTER               */
+  int32_t p2_steps;           /* Phase II (window) steps                         */
+  int32_t w_start, w_min;     /* window side at the first / last Phase II step   */
+  int32_t halo;               /* Halo width in tokens                            */
+  int32_t bridge_k;           /* bridge tokens per (batch, head); 0 = no bridge  */
+  int32_t split_num, split_den; /* smooth-window threshold (1/2)                 */
+  uint64_t seed;              /* seeds the per-step window-boundary shift        */
+} area_problem;
+
+typedef struct area_step {
+  int32_t phase;              /* AREA_PHASE_*                                    */
+  int32_t f;                  /* pooling factor of a coarse step, else 0        */
+  int32_t w;                  /* window side of a window step, else 0           */
+  int32_t ny, nx;             /* base windows per axis                           */
+  int32_t jit_y, jit_x;       /* boundary shift per axis                         */
+  int32_t max_windows;        /* upper bound on windows after splits (4 ny nx)   */
+  int64_t q_total;            /* sum of base-window query areas                  */
+} area_step;
+
+/* ---- host-only calls (no GPU needed) ------------------------------------ */
+
+/* Checks a problem: sizes positive, D in {64, 128}, T == 0, both grid sides
+ * even, a common factor >= max(2, f_min) when the canvas exceeds native
+ * (README canvas rules), w_min <= w_start, window sides even and >= 2,
+ * bridge cells fit the grid, split_den > 0.  Returns AREA_OK or an error. */
+int area_validate(const area_problem* p);
+
+/* Phase and schedule of denoising step `step` (0-based, Phase I steps
+ * first): the pooling factor from the linear ramp f0 -> f_min snapped to
+ * common grid divisors (blog, "Las dos fases de AReA", Fase I, with the
+ * worked example at 4096^2), or the window side from the geometric shrink
+ * w_start -> w_min, the base tiling counts and the step's boundary shift
+ * (ai.info summary, Methodology, Phase II).  At or below native every step
+ * is AREA_PHASE_FULL. */
+int area_step_info(const area_problem* p, int step, area_step* out);
+
+/* First pooling factor (f0 from the problem, or derived from the native
+ * grid when p->f0 == 0).  Returns the factor or a negative status. */
+int area_f0(const area_problem* p);
+
+/* Base windows of Phase II step `step` (before quadrant splits) as
+ * (y0, x0, h, w) int32 quadruples in row-major order, written to the HOST
+ * array out[4 * cap].  Returns the window count, or a negative status
+ * (AREA_E_INVALID if cap is too small). */
+int area_base_windows(const area_problem* p, int step, int32_t* out, int cap);
+
+/* Bytes of device workspace needed by the calls of class `op`
+ * (AREA_OP_*), the maximum over all steps of the problem.  0 on error. */
+size_t area_workspace_bytes(const area_problem* p, int op);
+
+/* int32 words of the plan buffer for any step of the problem. */
+size_t area_plan_words(const area_problem* p);
+
+/* Human-readable text for a status, and the thread's last error detail. */
+const char* area_strerror(int status);
+const char* area_last_error(void);
+
+/* ---- device calls ------------------------------------------------------- */
+
+/* Phase I pooling (blog Fase I; ai.info summary Phase I; README Phase I
+ * bullet).  k, v: [B][H][Gh*Gw][D] bf16, un-rotated.  kp, vp: outputs
+ * [B][H][(Gh/f)*(Gw/f)][D] in IEEE fp16 (the attention operand type, three
+ * mantissa bits finer than bf16).  Block (by, bx) sits at index
+ * by*(Gw/f)+bx.
+ * kp = RoPE(pool(k)) at integer coarse position (by, bx); vp = pool(v).
+ * pool = mean of the block's f*f tokens (fp32 sum, one rounding) or the
+ * block-centre token per p->pool_mode.  f must divide Gh and Gw. */
+int area_pool_kv(const area_problem* p, int f, const void* k, const void* v,
+                 void* kp, void* vp, void* stream);
+
+/* Phase I cross-scale coarse attention (ai.info summary, Methodology,
+ * Phase I): out = softmax(RoPE(q at (y/f, x/f)) kp^T / sqrt(D)) vp for every
+ * full-resolution query.  q: [B][H][Gh*Gw][D] bf16 un-rotated; kp, vp as
+ * produced by area_pool_kv; out: [B][H][Gh*Gw][D] bf16.  Workspace:
+ * area_workspace_bytes(p, AREA_OP_COARSE). kp and vp are fp16 as produced by
+ * area_pool_kv. */
+int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp,
+                     const void* vp, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Haar detail map (ai.info summary, Methodology, Phase II: a DWT map of the
+ * current state measures fine detail).  latent: [C][Gh][Gw] fp32.  For each
+ * 2x2 cell (a b / c d) and channel: LH = (a-b+c-d)/2, HL = (a+b-c-d)/2,
+ * HH = (a-b-c+d)/2, summed in float64 as E += (LH^2 + HL^2) + HH^2 in
+ * channel order.  energy: [Gh/2][Gw/2] fp32 (E rounded); energy_q:
+ * [Gh/2][Gw/2] int32 = min(round_half_even(E * 2^16), 2^31 - 1). */
+int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
+                    int32_t* energy_q, void* stream);
+
+/* Phase II window plan for step `step` (ai.info summary, Methodology,
+ * Phase II; README repository layout: tiling = base tiling, DWT map,
+ * splits, Halo, merge weights; bridge = bridge token selection).
+ *  energy_q: [Gh/2][Gw/2] int32 from area_dwt_detail (NULL: no splits).
+ *  k: [B][H][Gh*Gw][D] bf16 un-rotated keys, used for the bridge (NULL or
+ *     p->bridge_k == 0: no bridge).
+ * Outputs (device):
+ *  plan:   area_plan_words(p) int32: header + window records in canonical
+ *          order (row-major base windows; a split window replaced in place
+ *          by its quadrants TL, TR, BL, BR).  A base window is split when
+ *          split_den * S_w * N < split_num * S_tot * |Q_w|, S the integer
+ *          sums of energy_q over tokens.  Each record's key rectangle is its
+ *          query rectangle dilated by the Halo and clipped to the grid.
+ *  wsum:   [Gh*Gw] int32, sum over covering windows of the tent weight
+ *          min(u+1, L-u) along y times along x.
+ *  bridge_idx: [B][H][bridge_k] int32 sorted ascending: per (b, h), the key
+ *          farthest (sum of squared channel deviations, float64, channels in
+ *          order) from the exact mean key in each of bridge_k cells of a
+ *          r_h x r_w grid of the image; ties to the smaller index.
+ * Workspace: area_workspace_bytes(p, AREA_OP_PLAN). */
+int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, const void* k,
+                     int32_t* plan, int32_t* wsum, int32_t* bridge_idx,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Phase II windowed attention with blending (ai.info summary, Methodology,
+ * Phase II).  For every window of `plan`: its queries attend to the keys of
+ * its Halo rectangle plus the bridge tokens outside that rectangle, RoPE at
+ * native positions, softmax(q k^T / sqrt(D)) v; each token's output is the
+ * tent-weighted average of the outputs of the windows covering it (divided
+ * by wsum).  `step` must be the step the plan was built for.  q, k, v:
+ * [B][H][Gh*Gw][D] bf16 un-rotated; out: same layout.  bridge_idx may be
+ * NULL when the plan has R == 0.  Workspace:
+ * area_workspace_bytes(p, AREA_OP_WINDOW). */
+int area_window_attn(const area_problem* p, int step, const int32_t* plan, const int32_t* wsum,
+                     const int32_t* bridge_idx, const void* q, const void* k, const void* v,
+                     void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Uniform full attention over all Gh*Gw tokens with RoPE at native
+ * positions (the baseline of the pages' speedup figures, ai.info summary,
+ * Main Findings).  Same layouts as area_window_attn.  Workspace:
+ * area_workspace_bytes(p, AREA_OP_FULL). */
+int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v,
+                   void* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AREA_H */

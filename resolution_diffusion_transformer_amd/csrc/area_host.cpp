@@ -1,0 +1,505 @@
+// Host side of the AReA library: argument validation, the integer schedule
+// (pooling ramp, window shrink, base tiling, boundary shift), workspace
+// sizing and the C entry points that enqueue the kernels.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "area_internal.h"
+
+namespace area {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int gcd_int(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a < 0 ? -a : a;
+}
+
+int nearest_common_divisor(int a, int b, int lo, long long num, long long den) {
+  int g = gcd_int(a, b);
+  int best = -1;
+  long long bestd = 0;
+  for (int d = lo < 1 ? 1 : lo; d <= g; ++d) {
+    if (g % d) continue;
+    long long dist = (long long)d * den - num;
+    if (dist < 0) dist = -dist;
+    if (best < 0 || dist < bestd || (dist == bestd && d > best)) {
+      best = d;
+      bestd = dist;
+    }
+  }
+  return best;
+}
+
+// READING R5 (blog "Las dos fases de AReA", Fase I; ai.info summary,
+// Methodology, Phase I: f = 4 at 4096^2 maps the 256x256 grid to the native
+// 64x64): the common divisor >= f_min nearest to the larger grid/native
+// ratio, compared as exact fractions, ties to the larger divisor.
+int derive_f0(const area_problem& p) {
+  long long num, den;
+  if ((long long)p.Gh * p.native_w >= (long long)p.Gw * p.native_h) {
+    num = p.Gh;
+    den = p.native_h;
+  } else {
+    num = p.Gw;
+    den = p.native_w;
+  }
+  return nearest_common_divisor(p.Gh, p.Gw, p.f_min, num, den);
+}
+
+// READING R4: x_t = f0 + (f_min - f0) t / (P - 1), snapped to the nearest
+// common divisor >= f_min (ties to the larger), in exact integers.
+int ramp_factor(const area_problem& p, int f0, int t) {
+  int P = p.p1_steps;
+  if (P <= 1) return nearest_common_divisor(p.Gh, p.Gw, p.f_min, f0, 1);
+  long long den = P - 1;
+  long long num = (long long)f0 * den + (long long)(p.f_min - f0) * t;
+  return nearest_common_divisor(p.Gh, p.Gw, p.f_min, num, den);
+}
+
+// READING R6 (ai.info summary, Methodology, Phase II: geometric shrink from
+// w_start to w_min): r_t = w_start (w_min / w_start)^(t / (S - 1)) in
+// float64, then the nearest even integer, ties up.
+int window_side(const area_problem& p, int t) {
+  int S = p.p2_steps;
+  double r;
+  if (S <= 1) {
+    r = (double)p.w_start;
+  } else {
+    double ratio = (double)p.w_min / (double)p.w_start;
+    double e = (double)t / (double)(S - 1);
+    r = (double)p.w_start * std::pow(ratio, e);
+  }
+  return 2 * (int)std::floor(r / 2.0 + 0.5);
+}
+
+// READING R8 (ai.info summary, Phase II: evenly spaced base tiling):
+// n = ceil(G / w) windows (1 if w >= G), b_i = round_half_up(i (G-w)/(n-1)).
+void base_starts(int G, int w, std::vector<int>& out) {
+  out.clear();
+  if (w >= G) {
+    out.push_back(0);
+    return;
+  }
+  int n = (G + w - 1) / w;
+  for (int i = 0; i < n; ++i)
+    out.push_back((int)((2LL * i * (G - w) + (n - 1)) / (2LL * (n - 1))));
+}
+
+// SplitMix64 (Steele, Lea, Flood 2014): k-th output from state `seed`.
+uint64_t splitmix64(uint64_t seed, uint64_t k) {
+  uint64_t z = seed + k * 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// READING R9 (blog, Fase II and the tunables list: the seed drives the
+// border jitter): one shift per (step, axis) in [-J, J], J = half the
+// smallest overlap of neighbouring windows, applied to interior windows.
+int jitter_offset(const std::vector<int>& b, int L, uint64_t seed, int t, int axis) {
+  int n = (int)b.size();
+  if (n <= 2) return 0;
+  int gap = 0;
+  for (int i = 0; i + 1 < n; ++i) gap = std::max(gap, b[i + 1] - b[i]);
+  int ov = L - gap;
+  int J = ov > 0 ? ov / 2 : 0;
+  if (J == 0) return 0;
+  uint64_t r = splitmix64(seed, 2ULL * (uint64_t)t + (uint64_t)axis + 1ULL);
+  return (int)(r % (uint64_t)(2 * J + 1)) - J;
+}
+
+bool axis_tiling(int G, int w, uint64_t seed, int t, int axis, AxisTiling& out) {
+  std::vector<int> b;
+  base_starts(G, w, b);
+  if ((int)b.size() > kMaxAxisWindows) return false;
+  out.n = (int)b.size();
+  out.L = w < G ? w : G;
+  out.jitter = jitter_offset(b, out.L, seed, t, axis);
+  for (int i = 0; i < out.n; ++i) {
+    out.start[i] = b[i] + ((i > 0 && i < out.n - 1) ? out.jitter : 0);
+    if (out.start[i] < 0 || out.start[i] + out.L > G) return false;  // never: the shift keeps windows inside
+  }
+  return true;
+}
+
+// READING R13 (ai.info summary, Phase II: bridge tokens are spread
+// spatially): R cells on r_h x r_w, r_h the largest divisor of R with
+// r_h^2 Gw <= R Gh.
+bool bridge_cells(int R, int Gh, int Gw, int& rh, int& rw) {
+  int best = -1;
+  for (int d = 1; d <= R; ++d)
+    if (R % d == 0 && (long long)d * d * Gw <= (long long)R * Gh) best = d;
+  if (best < 0) return false;
+  rh = best;
+  rw = R / best;
+  return rh <= Gh && rw <= Gw;
+}
+
+// README canvas rules: at or below native the original attention is kept.
+bool canvas_gated(const area_problem& p) { return p.Gh <= p.native_h && p.Gw <= p.native_w; }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int window_step(const area_problem& p, int step, WindowStepInfo& out) {
+  if (canvas_gated(p)) return fail(AREA_E_INVALID, "canvas at or below native: no window steps");
+  int t = step - p.p1_steps;
+  if (step < 0 || t < 0 || t >= p.p2_steps)
+    return fail(AREA_E_INVALID, "step " + std::to_string(step) + " is not a Phase II step");
+  out.t = t;
+  out.w = window_side(p, t);
+  if (!axis_tiling(p.Gh, out.w, p.seed, t, 0, out.ty) ||
+      !axis_tiling(p.Gw, out.w, p.seed, t, 1, out.tx))
+    return fail(AREA_E_UNSUPPORTED, "more than 64 base windows per axis, or a window outside the grid");
+  int64_t nb = (int64_t)out.ty.n * out.tx.n;
+  int64_t Ly = out.ty.L, Lx = out.tx.L;
+  out.q_total = nb * Ly * Lx;
+  int64_t h1 = Ly / 2, w1 = Lx / 2;
+  int64_t unsplit = ceil_div(Ly * Lx, kAttnBM);
+  int64_t split = ceil_div(h1 * w1, kAttnBM) + ceil_div(h1 * (Lx - w1), kAttnBM) +
+                  ceil_div((Ly - h1) * w1, kAttnBM) + ceil_div((Ly - h1) * (Lx - w1), kAttnBM);
+  out.max_items = nb * (unsplit > split ? unsplit : split);
+  return AREA_OK;
+}
+
+static std::string pstr(const char* what, long long v) { return std::string(what) + "=" + std::to_string(v); }
+
+static int validate(const area_problem* pp) {
+  if (!pp) return fail(AREA_E_INVALID, "problem is NULL");
+  const area_problem& p = *pp;
+  if (p.B < 1 || p.H < 1 || p.Gh < 1 || p.Gw < 1 || p.native_h < 1 || p.native_w < 1)
+    return fail(AREA_E_INVALID, "B, H, Gh, Gw, native_h, native_w must be positive");
+  if (p.D != 64 && p.D != 128) return fail(AREA_E_UNSUPPORTED, pstr("head dim D must be 64 or 128, D", p.D));
+  if (p.T != 0) return fail(AREA_E_UNSUPPORTED, pstr("text tokens are not supported yet, T", p.T));
+  if (!(p.rope_theta > 0.0f) || !std::isfinite(p.rope_theta))
+    return fail(AREA_E_INVALID, "rope_theta must be positive and finite");
+  if (p.p1_steps < 0 || p.p2_steps < 0) return fail(AREA_E_INVALID, "step counts must be >= 0");
+  if (p.pool_mode != AREA_POOL_MEAN && p.pool_mode != AREA_POOL_CENTER)
+    return fail(AREA_E_INVALID, pstr("pool_mode", p.pool_mode));
+  if (p.f_min < 1 || p.f0 < 0) return fail(AREA_E_INVALID, "f_min must be >= 1 and f0 >= 0");
+  if (p.halo < 0 || p.bridge_k < 0) return fail(AREA_E_INVALID, "halo and bridge_k must be >= 0");
+  if (p.split_den <= 0 || p.split_num < 0) return fail(AREA_E_INVALID, "split_num >= 0, split_den > 0");
+  long long N = (long long)p.Gh * p.Gw;
+  if (N > (1LL << 30) || (long long)p.B * p.H * N * p.D > (1LL << 40))
+    return fail(AREA_E_UNSUPPORTED, "problem too large");
+  if (p.Gh % 2 || p.Gw % 2) return fail(AREA_E_SHAPE, "both grid sides must be even");
+  if (canvas_gated(p)) return AREA_OK;  // full attention only; the knobs below are unused
+  int fl = p.f_min > 2 ? p.f_min : 2;
+  if (gcd_int(p.Gh, p.Gw) < fl)
+    return fail(AREA_E_SHAPE, "grid sides share no factor >= max(2, f_min) (README canvas rules)");
+  if (p.f0 > 0 && (p.Gh % p.f0 || p.Gw % p.f0 || p.f0 < p.f_min))
+    return fail(AREA_E_SHAPE, pstr("f0 must be a common grid divisor >= f_min, f0", p.f0));
+  if (p.f0 == 0 && derive_f0(p) < 0) return fail(AREA_E_SHAPE, "no pooling factor fits the grid");
+  if (p.p2_steps > 0) {
+    if (p.w_min < 2 || p.w_start < p.w_min || p.w_min % 2 || p.w_start % 2)
+      return fail(AREA_E_SHAPE, "window sides must be even with 2 <= w_min <= w_start");
+    int nmax_y = (p.Gh + p.w_min - 1) / p.w_min, nmax_x = (p.Gw + p.w_min - 1) / p.w_min;
+    if (nmax_y > kMaxAxisWindows || nmax_x > kMaxAxisWindows)
+      return fail(AREA_E_UNSUPPORTED, "w_min gives more than 64 base windows per axis");
+    if (p.bridge_k > 0) {
+      int rh, rw;
+      if (!bridge_cells(p.bridge_k, p.Gh, p.Gw, rh, rw))
+        return fail(AREA_E_SHAPE, pstr("bridge cells do not fit the grid, bridge_k", p.bridge_k));
+      if (p.bridge_k > 4096) return fail(AREA_E_UNSUPPORTED, "bridge_k above 4096");
+    }
+  }
+  return AREA_OK;
+}
+
+static int64_t BH_of(const area_problem& p) { return (int64_t)p.B * p.H; }
+static int64_t N_of(const area_problem& p) { return (int64_t)p.Gh * p.Gw; }
+static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * N_of(p) * p.D * 2; }
+
+struct WindowMax {
+  int64_t q_total = 0, max_items = 0;
+  int max_windows = 0, n_base = 0;
+};
+
+static WindowMax window_max(const area_problem& p) {
+  WindowMax m;
+  for (int t = 0; t < p.p2_steps; ++t) {
+    WindowStepInfo wi;
+    if (window_step(p, p.p1_steps + t, wi) != AREA_OK) continue;
+    int nb = wi.ty.n * wi.tx.n;
+    m.q_total = std::max<int64_t>(m.q_total, wi.q_total);
+    m.max_items = std::max<int64_t>(m.max_items, wi.max_items);
+    m.max_windows = std::max(m.max_windows, 4 * nb);
+    m.n_base = std::max(m.n_base, nb);
+  }
+  return m;
+}
+
+static size_t workspace_bytes(const area_problem& p, int op) {
+  switch (op) {
+    case AREA_OP_FULL:
+      return 3 * align_up(tok_bytes(p));
+    case AREA_OP_COARSE:
+      return align_up(tok_bytes(p));
+    case AREA_OP_PLAN: {
+      if (canvas_gated(p) || p.p2_steps == 0) return 0;
+      WindowMax m = window_max(p);
+      return align_up(plan_ws_bytes(m.n_base)) +
+             align_up(bridge_ws_bytes(BH_of(p), (int)N_of(p), p.D, p.bridge_k));
+    }
+    case AREA_OP_WINDOW: {
+      if (canvas_gated(p) || p.p2_steps == 0) return 0;
+      WindowMax m = window_max(p);
+      return 3 * align_up(tok_bytes(p)) + align_up((size_t)m.q_total * BH_of(p) * p.D * 4) +
+             align_up(window_items_ws_bytes(m.max_windows, m.max_items, m.n_base));
+    }
+    default:
+      return 0;
+  }
+}
+
+static int check_ws(const area_problem& p, int op, void* ws, size_t ws_bytes) {
+  size_t need = workspace_bytes(p, op);
+  if (need == 0) return AREA_OK;
+  if (!ws) return fail(AREA_E_WORKSPACE, "workspace is NULL, need " + std::to_string(need) + " bytes");
+  if (ws_bytes < need)
+    return fail(AREA_E_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, need " +
+                                      std::to_string(need));
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(AREA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return AREA_OK;
+}
+
+}  // namespace area
+
+using namespace area;
+
+extern "C" {
+
+int area_validate(const area_problem* p) { return validate(p); }
+
+int area_f0(const area_problem* p) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (canvas_gated(*p)) return 1;
+  return p->f0 > 0 ? p->f0 : derive_f0(*p);
+}
+
+int area_step_info(const area_problem* p, int step, area_step* out) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!out) return fail(AREA_E_INVALID, "out is NULL");
+  std::memset(out, 0, sizeof(*out));
+  int total = p->p1_steps + p->p2_steps;
+  if (step < 0 || step >= total) return fail(AREA_E_INVALID, "step out of range");
+  if (canvas_gated(*p)) {
+    out->phase = AREA_PHASE_FULL;
+    return AREA_OK;
+  }
+  if (step < p->p1_steps) {
+    int f0 = p->f0 > 0 ? p->f0 : derive_f0(*p);
+    out->phase = AREA_PHASE_COARSE;
+    out->f = ramp_factor(*p, f0, step);
+    return AREA_OK;
+  }
+  WindowStepInfo wi;
+  rc = window_step(*p, step, wi);
+  if (rc) return rc;
+  out->phase = AREA_PHASE_WINDOW;
+  out->w = wi.w;
+  out->ny = wi.ty.n;
+  out->nx = wi.tx.n;
+  out->jit_y = wi.ty.jitter;
+  out->jit_x = wi.tx.jitter;
+  out->max_windows = 4 * wi.ty.n * wi.tx.n;
+  out->q_total = wi.q_total;
+  return AREA_OK;
+}
+
+int area_base_windows(const area_problem* p, int step, int32_t* out, int cap) {
+  int rc = validate(p);
+  if (rc) return rc;
+  WindowStepInfo wi;
+  rc = window_step(*p, step, wi);
+  if (rc) return rc;
+  int n = wi.ty.n * wi.tx.n;
+  if (!out || cap < n) return fail(AREA_E_INVALID, "output array too small: need " + std::to_string(n));
+  int k = 0;
+  for (int i = 0; i < wi.ty.n; ++i)
+    for (int j = 0; j < wi.tx.n; ++j) {
+      out[4 * k + 0] = wi.ty.start[i];
+      out[4 * k + 1] = wi.tx.start[j];
+      out[4 * k + 2] = wi.ty.L;
+      out[4 * k + 3] = wi.tx.L;
+      ++k;
+    }
+  return n;
+}
+
+size_t area_workspace_bytes(const area_problem* p, int op) {
+  if (validate(p)) return 0;
+  return workspace_bytes(*p, op);
+}
+
+size_t area_plan_words(const area_problem* p) {
+  if (validate(p) || canvas_gated(*p) || p->p2_steps == 0) return 0;
+  WindowMax m = window_max(*p);
+  return AREA_PLAN_HEADER + (size_t)AREA_PLAN_REC * m.max_windows;
+}
+
+const char* area_strerror(int status) {
+  switch (status) {
+    case AREA_OK: return "ok";
+    case AREA_E_INVALID: return "invalid argument";
+    case AREA_E_SHAPE: return "inconsistent shape";
+    case AREA_E_UNSUPPORTED: return "unsupported configuration";
+    case AREA_E_WORKSPACE: return "workspace missing or too small";
+    case AREA_E_HIP: return "HIP runtime failure";
+    default: return "unknown status";
+  }
+}
+
+const char* area_last_error(void) { return g_last_error.c_str(); }
+
+int area_pool_kv(const area_problem* p, int f, const void* k, const void* v, void* kp, void* vp,
+                 void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!k || !v || !kp || !vp) return fail(AREA_E_INVALID, "NULL tensor");
+  if (f < 1 || p->Gh % f || p->Gw % f) return fail(AREA_E_SHAPE, pstr("f must divide both grid sides, f", f));
+  return launch_pool(k, v, kp, vp, BH_of(*p), p->Gh, p->Gw, p->D, f, p->pool_mode, p->rope_theta, stream);
+}
+
+int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp, const void* vp,
+                     void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!q || !kp || !vp || !out) return fail(AREA_E_INVALID, "NULL tensor");
+  if (f < 1 || p->Gh % f || p->Gw % f) return fail(AREA_E_SHAPE, pstr("f must divide both grid sides, f", f));
+  rc = check_ws(*p, AREA_OP_COARSE, ws, ws_bytes);
+  if (rc) return rc;
+  int64_t BH = BH_of(*p);
+  int N = (int)N_of(*p);
+  int M = N / (f * f);
+  rc = launch_prep(q, nullptr, nullptr, ws, nullptr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
+                   stream);
+  if (rc) return rc;
+  return launch_dense_attn(ws, kp, vp, out, BH, N, M, p->D, stream);
+}
+
+int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
+  rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
+  if (rc) return rc;
+  int64_t BH = BH_of(*p);
+  int N = (int)N_of(*p);
+  char* qr = (char*)ws;
+  char* kr = qr + align_up(tok_bytes(*p));
+  char* vr = kr + align_up(tok_bytes(*p));
+  rc = launch_prep(q, k, v, qr, kr, vr, BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  if (rc) return rc;
+  return launch_dense_attn(qr, kr, vr, out, BH, N, N, p->D, stream);
+}
+
+int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
+                    int32_t* energy_q, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (C < 1) return fail(AREA_E_INVALID, "C must be >= 1");
+  if (!latent || !energy || !energy_q) return fail(AREA_E_INVALID, "NULL tensor");
+  return launch_dwt(latent, energy, energy_q, C, p->Gh, p->Gw, stream);
+}
+
+int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, const void* k,
+                     int32_t* plan, int32_t* wsum, int32_t* bridge_idx, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  WindowStepInfo wi;
+  rc = window_step(*p, step, wi);
+  if (rc) return rc;
+  if (!plan || !wsum) return fail(AREA_E_INVALID, "NULL plan or wsum");
+  bool use_bridge = p->bridge_k > 0 && k != nullptr;
+  if (use_bridge && !bridge_idx) return fail(AREA_E_INVALID, "bridge_idx is NULL");
+  rc = check_ws(*p, AREA_OP_PLAN, ws, ws_bytes);
+  if (rc) return rc;
+  PlanArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Gh = p->Gh;
+  a.Gw = p->Gw;
+  a.halo = p->halo;
+  a.R = use_bridge ? p->bridge_k : 0;
+  a.split_num = p->split_num;
+  a.split_den = energy_q ? p->split_den : 0;  // 0: never split
+  a.t = wi.t;
+  a.w = wi.w;
+  a.ny = wi.ty.n;
+  a.nx = wi.tx.n;
+  a.jit_y = wi.ty.jitter;
+  a.jit_x = wi.tx.jitter;
+  a.Ly = wi.ty.L;
+  a.Lx = wi.tx.L;
+  for (int i = 0; i < a.ny; ++i) a.ys[i] = wi.ty.start[i];
+  for (int i = 0; i < a.nx; ++i) a.xs[i] = wi.tx.start[i];
+  WindowMax m = window_max(*p);
+  char* wsb = (char*)ws;
+  rc = launch_plan(a, energy_q, plan, wsum, wsb, stream);
+  if (rc) return rc;
+  if (use_bridge) {
+    int rh, rw;
+    bridge_cells(p->bridge_k, p->Gh, p->Gw, rh, rw);
+    rc = launch_bridge(k, bridge_idx, BH_of(*p), p->Gh, p->Gw, p->D, p->bridge_k, rh, rw,
+                       wsb + align_up(plan_ws_bytes(m.n_base)), stream);
+  }
+  return rc;
+}
+
+int area_window_attn(const area_problem* p, int step, const int32_t* plan, const int32_t* wsum,
+                     const int32_t* bridge_idx, const void* q, const void* k, const void* v,
+                     void* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  WindowStepInfo wi;
+  rc = window_step(*p, step, wi);
+  if (rc) return rc;
+  if (!plan || !wsum || !q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
+  rc = check_ws(*p, AREA_OP_WINDOW, ws, ws_bytes);
+  if (rc) return rc;
+  WindowMax m = window_max(*p);
+  WindowAttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Gh = p->Gh;
+  a.Gw = p->Gw;
+  a.D = p->D;
+  a.R = (bridge_idx && p->bridge_k > 0) ? p->bridge_k : 0;
+  a.BH = BH_of(*p);
+  a.max_windows = 4 * wi.ty.n * wi.tx.n;
+  a.max_items = wi.max_items;
+  a.ny = wi.ty.n;
+  a.nx = wi.tx.n;
+  a.Ly = wi.ty.L;
+  a.Lx = wi.tx.L;
+  for (int i = 0; i < a.ny; ++i) a.ys[i] = wi.ty.start[i];
+  for (int i = 0; i < a.nx; ++i) a.xs[i] = wi.tx.start[i];
+  char* qr = (char*)ws;
+  char* kr = qr + align_up(tok_bytes(*p));
+  char* vr = kr + align_up(tok_bytes(*p));
+  float* slots = (float*)(vr + align_up(tok_bytes(*p)));
+  char* items = (char*)slots + align_up((size_t)m.q_total * BH_of(*p) * p->D * 4);
+  rc = launch_prep(q, k, v, qr, kr, vr, a.BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  if (rc) return rc;
+  return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, qr, kr, vr, out, items, slots,
+                            stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations shared by the host code and the kernel launchers of
+// the AReA library.  Nothing here is part of the public ABI (include/area.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "area.h"
+
+namespace area {
+
+// ---------------------------------------------------------------- errors --
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+// ------------------------------------------------------- fixed constants --
+constexpr int kMaxAxisWindows = 64;    // base windows per axis (kernel-argument table)
+constexpr int kAttnBM = 256;           // queries per attention work item
+constexpr int kAttnBN = 64;            // keys per staged tile
+constexpr int kBridgeChunk = 1024;     // rows per partial mean-key sum
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// --------------------------------------------------------- schedule math --
+// All plan decisions are integer or fixed-order float64 so that any other
+// implementation of the same steps reproduces them exactly.
+
+int gcd_int(int a, int b);
+// Common divisor d >= lo of (a, b) nearest to num/den, ties to the larger;
+// -1 if none.
+int nearest_common_divisor(int a, int b, int lo, long long num, long long den);
+int derive_f0(const area_problem& p);              // READING R5
+int ramp_factor(const area_problem& p, int f0, int t);  // READING R4
+int window_side(const area_problem& p, int t);     // READING R6
+void base_starts(int G, int w, std::vector<int>& out);  // READING R8
+uint64_t splitmix64(uint64_t seed, uint64_t k);
+int jitter_offset(const std::vector<int>& starts, int L, uint64_t seed, int t, int axis);  // R9
+
+struct AxisTiling {
+  int n = 0;
+  int L = 0;          // window extent along the axis (min(w, G))
+  int jitter = 0;
+  int start[kMaxAxisWindows];
+};
+// Base tiling + shift of one axis for Phase II step t; false if more than
+// kMaxAxisWindows windows would be needed.
+bool axis_tiling(int G, int w, uint64_t seed, int t, int axis, AxisTiling& out);
+
+bool bridge_cells(int R, int Gh, int Gw, int& rh, int& rw);  // READING R13
+
+bool canvas_gated(const area_problem& p);  // at or below native: full attention
+
+// Base-window statistics of a Phase II step used to size launches.
+struct WindowStepInfo {
+  int t = 0;                 // Phase II step index
+  int w = 0;
+  AxisTiling ty, tx;
+  int64_t q_total = 0;       // sum of query areas (== with splits)
+  int64_t max_items = 0;     // work items (window, query tile) over all split choices
+};
+int window_step(const area_problem& p, int step, WindowStepInfo& out);
+
+// ---------------------------------------------------------- launchers ----
+// Each returns AREA_OK or AREA_E_HIP (with the error text set).  Arguments
+// have been validated by the caller.
+typedef void* stream_t;
+
+// fp16 attention operands: qo = RoPE(q), ko = RoPE(k) at grid positions
+// (row / div, column / div), vo = v; k/ko and v/vo may be null.
+int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
+                int Gh, int Gw, int D, float theta, float div, stream_t s);
+int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int Gh, int Gw,
+                int D, int f, int mode, float theta, stream_t s);
+int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int Gh, int Gw,
+               stream_t s);
+
+struct PlanArgs {
+  int Gh, Gw, halo, R, split_num, split_den, t, w;
+  int ny, nx, jit_y, jit_x, Ly, Lx;
+  int ys[kMaxAxisWindows];
+  int xs[kMaxAxisWindows];
+};
+int launch_plan(const PlanArgs& a, const int32_t* energy_q, int32_t* plan, int32_t* wsum,
+                void* ws, stream_t s);
+size_t plan_ws_bytes(int n_base);
+
+int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D, int R, int rh,
+                  int rw, void* ws, stream_t s);
+size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
+
+// Attention over fp16 operands (rotated q and k, v), bf16 output.
+int launch_dense_attn(const void* q_rot, const void* k_rot, const void* v, void* out, int64_t BH,
+                      int Nq, int Nk, int D, stream_t s);
+
+struct WindowAttnArgs {
+  int Gh, Gw, D, R;
+  int64_t BH;
+  int max_windows;
+  int64_t max_items;
+  int ny, nx;
+  int ys[kMaxAxisWindows], xs[kMaxAxisWindows];
+  int Ly, Lx;
+};
+int launch_window_attn(const WindowAttnArgs& a, const int32_t* plan, const int32_t* wsum,
+                       const int32_t* bridge_idx, const void* q_rot, const void* k_rot,
+                       const void* v, void* out, void* items_ws, float* slots, stream_t s);
+size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base);
+
+}  // namespace area

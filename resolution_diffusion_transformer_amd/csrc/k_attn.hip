@@ -1,0 +1,661 @@
+// Flash-style attention on gfx950 for the AReA path: dense (full attention,
+// Phase I coarse attention over pooled keys) and windowed (Phase II: Halo
+// rectangle + bridge keys, tent-weighted blending of overlaps).
+//
+// Design (CDNA4, wave64):
+//  * MFMA v_mfma_f32_32x32x16_f16 with fp32 accumulation for both Q K^T and
+//    P V.  The operands (rotated Q and K, V, P) are IEEE fp16: the same MFMA
+//    rate as bf16 with three more mantissa bits, so the bf16 rounding of the
+//    output is the only coarse rounding on the path.
+//  * The score tile is computed transposed, S^T = K Q^T, so that each lane
+//    owns one query column: the softmax max/sum over keys is an in-lane
+//    reduction plus one exchange with the partner lane (lane ^ 32).
+//  * K rows are read in a permuted order so that the S^T accumulator
+//    registers already form the bf16 B operand of O^T += V^T P^T; P never
+//    leaves registers.
+//  * K (row-major) and V (transposed) tiles of 64 keys are staged through
+//    LDS, double-buffered, with the next tile's global loads in flight while
+//    the current tile is computed; one barrier per tile.
+//  * Online softmax in exp2 units with lazy rescaling: the running maximum
+//    only moves when a new score exceeds it by more than 2^8, so the O
+//    rescale is skipped on almost every tile.
+//  * Work items are mapped XCD-aware: consecutive items (same head, same
+//    window) land on the same XCD and share its L2.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <string>
+
+#include "area_internal.h"
+
+namespace area {
+
+namespace {
+
+typedef unsigned short u16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BN = kAttnBN;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(AREA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return AREA_OK;
+}
+
+struct AttnArgs {
+  const u16* q;        // rotated queries, fp16 [BH][Nq][D]
+  const u16* k;        // rotated keys, fp16 [BH][Nk][D]   (window mode: [BH][N][D])
+  const u16* v;        // values, fp16 [BH][Nk][D]
+  u16* out;            // [BH][Nq][D]
+  int64_t BH;
+  int Nq, Nk;          // dense mode sizes
+  int n_qtiles;        // dense mode: query tiles per head
+  int grid;            // launched work-groups (multiple of 8)
+  float c;             // log2(e) / sqrt(D)
+  // window mode
+  const int32_t* plan;
+  const int32_t* wsum;
+  const int32_t* bridge;   // [BH][R] or null
+  const int* items;        // [max_items][2] = (record, query tile)
+  const int* n_items;
+  const int* slot_off;     // per record: first slot of its query rect
+  float* slots;            // [slot][BH][D] fp32 outputs of overlapped tokens
+  int Gw, R;
+  int64_t max_items;
+};
+
+__device__ inline u16 f2bf(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+struct WinRect {
+  int qy0, qx0, qh, qw, ky0, kx0, kh, kw;
+};
+
+// Token of key slot s of a window (Halo rectangle first, then the bridge
+// list); bridge tokens inside the rectangle are invalid (already present).
+__device__ inline int win_key(int s, const WinRect& r, int Gw, const int32_t* br, int R, bool& valid) {
+  int nrect = r.kh * r.kw;
+  if (s < nrect) {
+    valid = true;
+    int yy = s / r.kw;
+    return (r.ky0 + yy) * Gw + r.kx0 + (s - yy * r.kw);
+  }
+  int j = s - nrect;
+  if (j < R) {
+    int tok = br[j];
+    int y = tok / Gw, x = tok - (tok / Gw) * Gw;
+    valid = !(y >= r.ky0 && y < r.ky0 + r.kh && x >= r.kx0 && x < r.kx0 + r.kw);
+    return tok;
+  }
+  valid = false;
+  return 0;
+}
+
+template <int D, int NW, int QG, bool WIN>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32 * QG;
+  constexpr int KD = D / 16;      // MFMA k-steps over the head dim (QK^T)
+  constexpr int DB = D / 32;      // 32-row blocks of O^T
+  constexpr int KS = D + 8;       // K tile row stride in LDS (bf16), breaks bank aliasing
+  constexpr int VS = BN + 8;      // V^T tile row stride in LDS
+  constexpr int CPR = D / 8;      // 16-byte chunks per token row
+  constexpr int K_CPT = BN * CPR / NT;
+  constexpr int VK = 8 * D / NT;  // keys per V^T store group
+  static_assert(K_CPT >= 1 && BN * CPR == K_CPT * NT, "K tile split");
+  static_assert(VK >= 1 && (BN / VK) * CPR == NT, "V tile split");
+
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * KS];
+  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hi = lane >> 5;
+
+  // ---- work item (XCD-aware order: logical ids are contiguous per XCD)
+  const int pid = blockIdx.x;
+  const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
+  int64_t bh;
+  int qtile = 0, rec = 0;
+  WinRect r = {0, 0, 0, 0, 0, 0, 0, 0};
+  int nq, nkv;
+  if constexpr (WIN) {
+    bh = L / a.max_items;
+    int64_t it = L - bh * a.max_items;
+    if (bh >= a.BH || it >= *a.n_items) return;
+    rec = a.items[2 * it];
+    qtile = a.items[2 * it + 1];
+    const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
+    r.qy0 = rp[0]; r.qx0 = rp[1]; r.qh = rp[2]; r.qw = rp[3];
+    r.ky0 = rp[4]; r.kx0 = rp[5]; r.kh = rp[6]; r.kw = rp[7];
+    nq = r.qh * r.qw;
+    nkv = r.kh * r.kw + a.R;
+  } else {
+    bh = L / a.n_qtiles;
+    qtile = (int)(L - bh * a.n_qtiles);
+    if (bh >= a.BH) return;
+    nq = a.Nq;
+    nkv = a.Nk;
+  }
+  const int32_t* br = (WIN && a.R > 0) ? a.bridge + bh * a.R : nullptr;
+  const int64_t kv_rows = WIN ? 0 : (int64_t)a.Nk;
+  const u16* kbase = a.k + bh * (WIN ? (int64_t)a.Nq : kv_rows) * D;
+  const u16* vbase = a.v + bh * (WIN ? (int64_t)a.Nq : kv_rows) * D;
+  const u16* qbase = a.q + bh * (int64_t)a.Nq * D;
+
+  // ---- queries of this lane
+  int qtok[QG];
+  bool qvalid[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    int t = qtile * BM + wave * 32 * QG + 32 * g + n;
+    qvalid[g] = t < nq;
+    if constexpr (WIN) {
+      int yy = qvalid[g] ? t / r.qw : 0;
+      int xx = qvalid[g] ? t - yy * r.qw : 0;
+      qtok[g] = (r.qy0 + yy) * a.Gw + r.qx0 + xx;
+    } else {
+      qtok[g] = qvalid[g] ? t : 0;
+    }
+  }
+  f16x8 qf[QG][KD];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const f16x8* qrow = reinterpret_cast<const f16x8*>(qbase + (int64_t)qtok[g] * D);
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd) qf[g][kd] = qrow[2 * kd + hi];
+  }
+
+  const int ntiles = (nkv + BN - 1) / BN;
+
+  // ---- global -> register prefetch of one K/V tile
+  uint4 kreg[K_CPT];
+  uint4 vreg[VK];
+  auto key_tok = [&](int s, bool& valid) -> int {
+    if constexpr (WIN) {
+      return win_key(s, r, a.Gw, br, a.R, valid);
+    } else {
+      valid = s < nkv;
+      return valid ? s : 0;
+    }
+  };
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < K_CPT; ++i) {
+      int c = tid + i * NT;
+      int row = c / CPR, col = c - row * CPR;
+      bool ok;
+      int tok = key_tok(j * BN + row, ok);
+      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)tok * D + col * 8);
+    }
+    {
+      int dc = tid % CPR, kg = tid / CPR;
+#pragma unroll
+      for (int q = 0; q < VK; ++q) {
+        bool ok;
+        int tok = key_tok(j * BN + kg * VK + q, ok);
+        vreg[q] = *reinterpret_cast<const uint4*>(vbase + (int64_t)tok * D + dc * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < K_CPT; ++i) {
+      int c = tid + i * NT;
+      int row = c / CPR, col = c - row * CPR;
+      *reinterpret_cast<uint4*>(&Ks[st][row * KS + col * 8]) = kreg[i];
+    }
+    int dc = tid % CPR, kg = tid / CPR;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      u16 e[VK];
+#pragma unroll
+      for (int q = 0; q < VK; ++q) {
+        const unsigned w[4] = {vreg[q].x, vreg[q].y, vreg[q].z, vreg[q].w};
+        e[q] = (u16)((jd & 1) ? (w[jd >> 1] >> 16) : (w[jd >> 1] & 0xFFFFu));
+      }
+      u16* dst = &Vt[st][(dc * 8 + jd) * VS + kg * VK];
+      if constexpr (VK == 4) {
+        uint2 pk = make_uint2((unsigned)e[0] | ((unsigned)e[1] << 16), (unsigned)e[2] | ((unsigned)e[3] << 16));
+        *reinterpret_cast<uint2*>(dst) = pk;
+      } else if constexpr (VK == 2) {
+        *reinterpret_cast<unsigned*>(dst) = (unsigned)e[0] | ((unsigned)e[1] << 16);
+      } else {
+#pragma unroll
+        for (int q = 0; q < VK; ++q) dst[q] = e[q];
+      }
+    }
+  };
+
+  // ---- accumulators
+  f32x16 o[QG][DB];
+  float m_run[QG], l_run[QG];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[g][db][i] = 0.0f;
+  }
+  const float c = a.c;
+  // K row read by MFMA row n (swaps bits 2 and 3) so that S^T registers
+  // 8*jj + i of block kb hold key 32 kb + 16 jj + 8 hi + i.
+  const int krow_perm = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int st = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+
+    // validity of the tile's 64 keys (identical for every query)
+    uint64_t vm;
+    {
+      bool ok;
+      (void)key_tok(j * BN + lane, ok);
+      vm = __ballot(ok);
+    }
+    const bool full = (vm == ~0ull);
+    const uint32_t lm = (uint32_t)(vm >> (8 * hi)) & 0x00FF00FFu;   // bits 0..7, 16..23 used per block
+    const uint32_t lm_hi = (uint32_t)(vm >> (32 + 8 * hi)) & 0x00FF00FFu;
+
+    const u16* ks = Ks[st];
+    const u16* vt = Vt[st];
+
+    f32x16 s[QG][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int g = 0; g < QG; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
+      const u16* kr = ks + (32 * kb + krow_perm) * KS + 8 * hi;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) {
+        f16x8 af = *reinterpret_cast<const f16x8*>(kr + 16 * kd);
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+          s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, qf[g][kd], s[g][kb], 0, 0, 0);
+      }
+    }
+
+    f16x8 pf[QG][4];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          uint32_t bits = kb ? lm_hi : lm;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            int bit = 16 * (i >> 3) + (i & 7);
+            if (!((bits >> bit) & 1u)) s[g][kb][i] = -INFINITY;
+          }
+        }
+      }
+      float mx = s[g][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mc = mx * c;
+      const bool need = mc > m_run[g] + kLazy;
+      if (__any(need)) {
+        const float m_new = need ? mc : m_run[g];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
+        m_run[g] = m_new;
+      }
+      const float negm = -m_run[g];
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f16x8 pv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][kb][8 * hh + i], c, negm));
+            ls += p;
+            pv[i] = (_Float16)p;
+          }
+          pf[g][2 * kb + hh] = pv;
+        }
+      }
+      l_run[g] += ls;
+    }
+
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
+      const u16* vr = vt + n * VS + 16 * ks2 + 8 * hi;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f16x8 af = *reinterpret_cast<const f16x8*>(vr + 32 * db * VS);
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+          o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[g][ks2], o[g][db], 0, 0, 0);
+      }
+    }
+
+    if (j + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise and write
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    float lt = l_run[g] + __shfl_xor(l_run[g], 32);
+    float inv = 1.0f / lt;
+    if (!qvalid[g]) continue;
+    if constexpr (WIN) {
+      int t = qtile * BM + wave * 32 * QG + 32 * g + n;
+      int uy = t / r.qw, ux = t - (t / r.qw) * r.qw;
+      int wt = min(uy + 1, r.qh - uy) * min(ux + 1, r.qw - ux);
+      int tok = qtok[g];
+      if (a.wsum[tok] == wt) {
+        u16* orow = a.out + (bh * (int64_t)a.Nq + tok) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            int d = 32 * db + 8 * q4 + 4 * hi;
+            uint2 pk;
+            pk.x = (unsigned)f2bf(o[g][db][4 * q4 + 0] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 1] * inv) << 16);
+            pk.y = (unsigned)f2bf(o[g][db][4 * q4 + 2] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 3] * inv) << 16);
+            *reinterpret_cast<uint2*>(orow + d) = pk;
+          }
+      } else {
+        float* srow = a.slots + ((int64_t)(a.slot_off[rec] + t) * a.BH + bh) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            int d = 32 * db + 8 * q4 + 4 * hi;
+            float4 v4 = make_float4(o[g][db][4 * q4 + 0] * inv, o[g][db][4 * q4 + 1] * inv,
+                                    o[g][db][4 * q4 + 2] * inv, o[g][db][4 * q4 + 3] * inv);
+            *reinterpret_cast<float4*>(srow + d) = v4;
+          }
+      }
+    } else {
+      u16* orow = a.out + (bh * (int64_t)a.Nq + qtok[g]) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int d = 32 * db + 8 * q4 + 4 * hi;
+          uint2 pk;
+          pk.x = (unsigned)f2bf(o[g][db][4 * q4 + 0] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 1] * inv) << 16);
+          pk.y = (unsigned)f2bf(o[g][db][4 * q4 + 2] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + d) = pk;
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------ work list --
+// Items workspace: [0] n_items, then slot_off[max_windows],
+// rec_start[n_base], items[max_items][2].
+struct ItemsWs {
+  int* n_items;
+  int* slot_off;
+  int* rec_start;
+  int* items;
+};
+
+ItemsWs make_items_ws(void* ws, int max_windows, int n_base) {
+  ItemsWs w;
+  char* p = (char*)ws;
+  w.n_items = (int*)p;
+  p += align_up(sizeof(int));
+  w.slot_off = (int*)p;
+  p += align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1));
+  w.rec_start = (int*)p;
+  p += align_up(sizeof(int) * (n_base > 0 ? n_base : 1));
+  w.items = (int*)p;
+  return w;
+}
+
+// One block: slot offsets (prefix of query areas in record order), the
+// first record of every base window, and the (record, query tile) list with
+// whole windows first and quadrants after (largest key sets first).
+__global__ __launch_bounds__(256) void items_kernel(const int32_t* __restrict__ plan, ItemsWs w, int BM,
+                                                    int max_windows, int64_t max_items) {
+  __shared__ int s_item_off[4 * kMaxAxisWindows * kMaxAxisWindows];
+  int nwin = plan[AREA_PH_NWIN];
+  if (nwin > max_windows) nwin = max_windows;
+  if (threadIdx.x == 0) {
+    int qs = 0, it = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int i = 0; i < nwin; ++i) {
+        const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+        bool quad = rp[9] >= 0;
+        if ((pass == 0) == quad) continue;
+        s_item_off[i] = it;
+        it += (rp[2] * rp[3] + BM - 1) / BM;
+      }
+    }
+    for (int i = 0; i < nwin; ++i) {
+      const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+      w.slot_off[i] = qs;
+      qs += rp[2] * rp[3];
+      if (rp[9] <= 0) w.rec_start[rp[8]] = i;
+    }
+    if (it > max_items) it = (int)max_items;
+    *w.n_items = it;
+  }
+  __syncthreads();
+  for (int i = 0; i < nwin; ++i) {
+    const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+    int nt = (rp[2] * rp[3] + BM - 1) / BM;
+    for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+      int idx = s_item_off[i] + t;
+      if (idx < max_items) {
+        w.items[2 * idx] = i;
+        w.items[2 * idx + 1] = t;
+      }
+    }
+  }
+}
+
+struct BlendArgs {
+  int Gh, Gw, D, ny, nx, Ly, Lx;
+  int64_t BH;
+  int ys[kMaxAxisWindows], xs[kMaxAxisWindows];
+};
+
+constexpr int kBlendTok = 16;
+constexpr int kMaxCover = 8;
+
+__device__ inline int tent_w(int u, int L) { return min(u + 1, L - u); }
+
+// Tokens covered by more than one window: out = sum_w wt_w * O_w / wsum,
+// windows in record order.
+__global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* __restrict__ plan,
+                                                    const int* __restrict__ rec_start, const int* __restrict__ slot_off,
+                                                    const int32_t* __restrict__ wsum, const float* __restrict__ slots,
+                                                    u16* __restrict__ out) {
+  __shared__ int s_slot[kMaxCover * kMaxCover];
+  __shared__ float s_wt[kMaxCover * kMaxCover];
+  __shared__ int s_cnt;
+  int64_t N = (int64_t)b.Gh * b.Gw;
+  int D4 = b.D / 4;
+  for (int k = 0; k < kBlendTok; ++k) {
+    int64_t p = (int64_t)blockIdx.x * kBlendTok + k;
+    if (p >= N) break;
+    int y = (int)(p / b.Gw), x = (int)(p % b.Gw);
+    if (threadIdx.x == 0) {
+      int iy[kMaxCover], ix[kMaxCover], cy = 0, cx = 0;
+      for (int i = 0; i < b.ny; ++i)
+        if (y >= b.ys[i] && y < b.ys[i] + b.Ly && cy < kMaxCover) iy[cy++] = i;
+      for (int j = 0; j < b.nx; ++j)
+        if (x >= b.xs[j] && x < b.xs[j] + b.Lx && cx < kMaxCover) ix[cx++] = j;
+      int cnt = 0;
+      if (cy * cx > 1) {
+        for (int a = 0; a < cy; ++a)
+          for (int c = 0; c < cx; ++c) {
+            int r0 = rec_start[iy[a] * b.nx + ix[c]];
+            int rr = r0;
+            const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * r0;
+            if (rp[9] >= 0) {
+              // split window: pick the quadrant holding (y, x)
+              for (int qd = 0; qd < 4; ++qd) {
+                const int32_t* qp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * (r0 + qd);
+                if (y >= qp[0] && y < qp[0] + qp[2] && x >= qp[1] && x < qp[1] + qp[3]) rr = r0 + qd;
+              }
+            }
+            const int32_t* wp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rr;
+            int uy = y - wp[0], ux = x - wp[1];
+            s_wt[cnt] = (float)(tent_w(uy, wp[2]) * tent_w(ux, wp[3]));
+            s_slot[cnt] = slot_off[rr] + uy * wp[3] + ux;
+            ++cnt;
+          }
+      }
+      s_cnt = cnt;
+    }
+    __syncthreads();
+    int cnt = s_cnt;
+    if (cnt > 1) {
+      float inv = 1.0f / (float)wsum[p];
+      for (int e = threadIdx.x; e < b.BH * D4; e += blockDim.x) {
+        int64_t bh = e / D4;
+        int d4 = e - (int)bh * D4;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < cnt; ++i) {
+          float4 v = *reinterpret_cast<const float4*>(slots + ((int64_t)s_slot[i] * b.BH + bh) * b.D + 4 * d4);
+          float wgt = s_wt[i];
+          acc.x += wgt * v.x;
+          acc.y += wgt * v.y;
+          acc.z += wgt * v.z;
+          acc.w += wgt * v.w;
+        }
+        uint2 pk;
+        pk.x = (unsigned)f2bf(acc.x * inv) | ((unsigned)f2bf(acc.y * inv) << 16);
+        pk.y = (unsigned)f2bf(acc.z * inv) | ((unsigned)f2bf(acc.w * inv) << 16);
+        *reinterpret_cast<uint2*>(out + (bh * N + p) * b.D + 4 * d4) = pk;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Kernel shape: waves per work-group and 32-query groups per wave (the
+// product times 32 is the query tile, 256).  AREA_ATTN_SHAPE=4x2 or 8x1
+// selects one for measurement; 4x2 is the default.
+int attn_shape() {
+  static int shape = [] {
+    const char* e = std::getenv("AREA_ATTN_SHAPE");
+    if (e && std::string(e) == "8x1") return 1;
+    return 0;
+  }();
+  return shape;
+}
+
+template <bool WIN>
+int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
+  AttnArgs b = a;
+  int64_t g = (work + 7) / 8 * 8;
+  if (g > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "attention grid too large");
+  b.grid = (int)g;
+  dim3 grid((unsigned)b.grid);
+  if (D == 128) {
+    if (attn_shape() == 1)
+      hipLaunchKernelGGL((attn_kernel<128, 8, 1, WIN>), grid, dim3(512), 0, st, b);
+    else
+      hipLaunchKernelGGL((attn_kernel<128, 4, 2, WIN>), grid, dim3(256), 0, st, b);
+  } else {
+    if (attn_shape() == 1)
+      hipLaunchKernelGGL((attn_kernel<64, 8, 1, WIN>), grid, dim3(512), 0, st, b);
+    else
+      hipLaunchKernelGGL((attn_kernel<64, 4, 2, WIN>), grid, dim3(256), 0, st, b);
+  }
+  return check_launch(WIN ? "attn_kernel<window>" : "attn_kernel<dense>");
+}
+
+}  // namespace
+
+int launch_dense_attn(const void* q_rot, const void* k_rot, const void* v, void* out, int64_t BH, int Nq,
+                      int Nk, int D, stream_t s) {
+  AttnArgs a = {};
+  a.q = (const u16*)q_rot;
+  a.k = (const u16*)k_rot;
+  a.v = (const u16*)v;
+  a.out = (u16*)out;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.n_qtiles = (Nq + kAttnBM - 1) / kAttnBM;
+  a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
+  return launch_attn<false>(a, D, (int64_t)a.n_qtiles * BH, (hipStream_t)s);
+}
+
+size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base) {
+  return align_up(sizeof(int)) + align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1)) +
+         align_up(sizeof(int) * (n_base > 0 ? n_base : 1)) + align_up(sizeof(int) * 2 * (max_items > 0 ? max_items : 1));
+}
+
+int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32_t* wsum, const int32_t* bridge_idx,
+                       const void* q_rot, const void* k_rot, const void* v, void* out, void* items_ws, float* slots,
+                       stream_t s) {
+  hipStream_t st = (hipStream_t)s;
+  int n_base = w.ny * w.nx;
+  ItemsWs iw = make_items_ws(items_ws, w.max_windows, n_base);
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(256), 0, st, plan, iw, kAttnBM, w.max_windows, w.max_items);
+  int rc = check_launch("items_kernel");
+  if (rc) return rc;
+  AttnArgs a = {};
+  a.q = (const u16*)q_rot;
+  a.k = (const u16*)k_rot;
+  a.v = (const u16*)v;
+  a.out = (u16*)out;
+  a.BH = w.BH;
+  a.Nq = w.Gh * w.Gw;
+  a.Nk = w.Gh * w.Gw;
+  a.c = (float)(1.4426950408889634 / std::sqrt((double)w.D));
+  a.plan = plan;
+  a.wsum = wsum;
+  a.bridge = bridge_idx;
+  a.items = iw.items;
+  a.n_items = iw.n_items;
+  a.slot_off = iw.slot_off;
+  a.slots = slots;
+  a.Gw = w.Gw;
+  a.R = bridge_idx ? w.R : 0;
+  a.max_items = w.max_items;
+  rc = launch_attn<true>(a, w.D, w.max_items * w.BH, st);
+  if (rc) return rc;
+  BlendArgs b;
+  b.Gh = w.Gh;
+  b.Gw = w.Gw;
+  b.D = w.D;
+  b.ny = w.ny;
+  b.nx = w.nx;
+  b.Ly = w.Ly;
+  b.Lx = w.Lx;
+  b.BH = w.BH;
+  for (int i = 0; i < kMaxAxisWindows; ++i) {
+    b.ys[i] = w.ys[i];
+    b.xs[i] = w.xs[i];
+  }
+  int64_t N = (int64_t)w.Gh * w.Gw;
+  hipLaunchKernelGGL(blend_kernel, dim3((unsigned)((N + kBlendTok - 1) / kBlendTok)), dim3(256), 0, st, b, plan,
+                     (const int*)iw.rec_start, (const int*)iw.slot_off, wsum, (const float*)slots, (u16*)out);
+  return check_launch("blend_kernel");
+}
+
+}  // namespace area

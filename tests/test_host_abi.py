@@ -1,0 +1,185 @@
+"""CPU tests of the C ABI: the library loads and exports every declared
+symbol, its host-side schedule and tiling match the oracle bit for bit, and
+invalid requests are rejected before anything is launched."""
+import ctypes
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import resolution_diffusion_transformer_amd as A
+import workloads as W
+from oracle import area_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(A.library_path()):
+        from resolution_diffusion_transformer_amd import _build
+        _build.build(verbose=False)
+    A.lib()
+
+
+def declared_symbols():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(inc, fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(area_[a-z0-9_]+)\s*\(", txt))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for must in ["area_pool_kv", "area_coarse_attn", "area_dwt_detail", "area_window_plan",
+                 "area_window_attn", "area_full_attn", "area_validate", "area_step_info",
+                 "area_workspace_bytes"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(A.library_path())
+    missing = [n for n in declared_symbols() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(declared_symbols()) == set(A.exported_symbols())
+
+
+def prob(name, **over):
+    return A.problem_for(W.get(name), **over)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_schedule_matches_oracle(name):
+    wl = W.get(name)
+    p = prob(name)
+    assert A.area_validate(p) == 0
+    f0 = O.f0_for(wl.Gh, wl.Gw, wl.native_h, wl.native_w, wl.f_min)
+    assert A.area_f0(p) == f0
+    ramp = O.pooling_ramp(wl.Gh, wl.Gw, f0, wl.f_min, wl.p1_steps)
+    ws = O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)
+    for s in range(wl.p1_steps):
+        info = A.area_step_info(p, s)
+        assert info["phase"] == A.PHASE_COARSE and info["f"] == ramp[s]
+    for t in range(wl.p2_steps):
+        s = wl.p1_steps + t
+        info = A.area_step_info(p, s)
+        ys, oy = O.axis_windows(wl.Gh, ws[t], wl.seed, t, 0)
+        xs, ox = O.axis_windows(wl.Gw, ws[t], wl.seed, t, 1)
+        assert info["phase"] == A.PHASE_WINDOW
+        assert (info["w"], info["ny"], info["nx"], info["jit_y"], info["jit_x"]) == \
+            (ws[t], len(ys), len(xs), oy, ox)
+        bw = A.area_base_windows(p, s)
+        expect = [(y0, x0, h, w) for (y0, h) in ys for (x0, w) in xs]
+        assert [tuple(r) for r in bw.tolist()] == expect
+
+
+def test_schedule_matches_oracle_random_problems():
+    rnd = random.Random(1234)
+    for _ in range(300):
+        Gh = 2 * rnd.randint(8, 200)
+        Gw = 2 * rnd.randint(8, 200)
+        nat = rnd.randint(4, min(Gh, Gw))
+        wmin = 2 * rnd.randint(1, 40)
+        wst = wmin + 2 * rnd.randint(0, 100)
+        P1, S = rnd.randint(0, 12), rnd.randint(0, 24)
+        seed = rnd.getrandbits(64)
+        p = A.Problem(B=1, H=1, D=64, Gh=Gh, Gw=Gw, native_h=nat, native_w=nat, p1_steps=P1,
+                      p2_steps=S, w_start=wst, w_min=wmin, halo=2, seed=seed)
+        try:
+            A.area_validate(p)
+        except A.AreaError:
+            continue
+        if Gh <= nat and Gw <= nat:
+            for s in range(P1 + S):
+                assert A.area_step_info(p, s)["phase"] == A.PHASE_FULL
+            continue
+        f0 = O.f0_for(Gh, Gw, nat, nat, 2)
+        assert A.area_f0(p) == f0
+        ramp = O.pooling_ramp(Gh, Gw, f0, 2, P1)
+        wsz = O.window_sizes(wst, wmin, S)
+        for s in range(P1):
+            assert A.area_step_info(p, s)["f"] == ramp[s]
+        for t in range(S):
+            info = A.area_step_info(p, P1 + t)
+            ys, oy = O.axis_windows(Gh, wsz[t], seed, t, 0)
+            xs, ox = O.axis_windows(Gw, wsz[t], seed, t, 1)
+            assert (info["w"], info["jit_y"], info["jit_x"]) == (wsz[t], oy, ox)
+            bw = A.area_base_windows(p, P1 + t)
+            assert [tuple(r) for r in bw.tolist()] == [(y0, x0, h, w) for (y0, h) in ys for (x0, w) in xs]
+
+
+def test_gated_canvas_keeps_full_attention():
+    p = A.Problem(B=1, H=2, D=128, Gh=64, Gw=64, native_h=64, native_w=64, p1_steps=8, p2_steps=4,
+                  w_start=64, w_min=32)
+    assert A.area_validate(p) == 0
+    for s in range(12):
+        assert A.area_step_info(p, s)["phase"] == A.PHASE_FULL
+    assert A.area_workspace_bytes(p, A.OP_WINDOW) == 0
+    assert A.area_workspace_bytes(p, A.OP_FULL) == 3 * p.B * p.H * p.N * p.D * 2
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=96), -3), (dict(T=4), -3), (dict(Gh=127), -2), (dict(Gh=130, Gw=126), 0),
+    (dict(Gh=2 * 67, Gw=2 * 71), 0),               # both even: they share the factor 2
+    (dict(w_start=60, w_min=64), -2), (dict(w_min=63), -2), (dict(bridge_k=3 * 1024 * 1024), -2),
+    (dict(pool_mode=7), -1), (dict(split_den=0), -1), (dict(halo=-1), -1), (dict(B=0), -1),
+    (dict(f0=5), -2), (dict(rope_theta=-1.0), -1),
+])
+def test_validation_statuses(over, status):
+    p = prob("flux-2048", **over)
+    if status == 0:
+        assert A.area_validate(p) == 0
+    else:
+        with pytest.raises(A.AreaError) as e:
+            A.area_validate(p)
+        assert e.value.status == status
+
+
+def test_odd_factor_grid_rejected():
+    # grid sides sharing no factor >= 2 (README canvas rules); even sides always share 2,
+    # so use f_min = 3 to ask for a factor the sides do not share
+    p = A.Problem(B=1, H=1, D=64, Gh=2 * 67, Gw=2 * 71, native_h=64, native_w=64, f_min=3)
+    with pytest.raises(A.AreaError) as e:
+        A.area_validate(p)
+    assert e.value.status == -2
+
+
+def test_device_calls_reject_bad_arguments_before_launch():
+    L = A.lib()
+    p = prob("flux-2048").c()
+    fake = ctypes.c_void_p(0x1000)
+    # NULL tensors
+    assert L.area_full_attn(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 40, None) == -1
+    assert L.area_pool_kv(ctypes.byref(p), 2, fake, None, fake, fake, None) == -1
+    # pooling factor that does not divide the grid
+    assert L.area_pool_kv(ctypes.byref(p), 3, fake, fake, fake, fake, None) == -2
+    # workspace too small / missing / misaligned
+    assert L.area_full_attn(ctypes.byref(p), fake, fake, fake, fake, fake, 16, None) == -4
+    assert L.area_full_attn(ctypes.byref(p), fake, fake, fake, fake, None, 1 << 40, None) == -4
+    assert L.area_full_attn(ctypes.byref(p), fake, fake, fake, fake, ctypes.c_void_p(0x1008), 1 << 40, None) == -4
+    # a coarse step index given to a window call
+    assert L.area_window_plan(ctypes.byref(p), 0, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    assert L.area_window_attn(ctypes.byref(p), 99, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None) == -1
+    assert b"Phase II" in L.area_last_error() or b"step" in L.area_last_error()
+    assert L.area_validate(None) == -1
+    assert L.area_strerror(-4) == b"workspace missing or too small"
+
+
+def test_workspace_sizes():
+    p = prob("flux-6144")
+    tok = p.B * p.H * p.N * p.D * 2
+    assert A.area_workspace_bytes(p, A.OP_FULL) == 3 * tok
+    assert A.area_workspace_bytes(p, A.OP_COARSE) == tok
+    # window workspace covers fp16 q, k, v operands and fp32 outputs of the largest step
+    wl = W.get("flux-6144")
+    qmax = max(len(O.axis_windows(wl.Gh, w, 0, t, 0)[0]) * len(O.axis_windows(wl.Gw, w, 0, t, 1)[0])
+               * min(w, wl.Gh) * min(w, wl.Gw)
+               for t, w in enumerate(O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)))
+    assert A.area_workspace_bytes(p, A.OP_WINDOW) >= 3 * tok + qmax * p.B * p.H * p.D * 4
+    assert A.area_plan_words(p) == A.PLAN_HEADER + A.PLAN_REC * 4 * 36
