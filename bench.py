@@ -1,0 +1,340 @@
+"""Benchmark of the AReA attention path on one MI355X.
+
+One bench step is one pass of the whole hot path for one attention layer of
+the FLUX.1-shaped 6144x6144 workload (384x384 tokens, 24 heads, head dim
+128): every denoising step of the schedule -- 8 coarse steps (pool + coarse
+attention over the pooling ramp) and 20 window steps (Haar map, window plan
+with bridge, windowed attention with blending) -- plus one uniform full
+attention call at the same shape, the baseline of the speedup.
+
+The reported value is AReA attention milliseconds per denoising step (the
+schedule's time divided by its 28 steps), timed over K bench steps after W
+warm-up steps with inputs already resident in HBM.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "AReA attn ms/step + % bf16 MFMA peak, FLUX-shape 6144²; speedup vs full attn"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def new(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        self.pool.append(ev.value)
+        return ev.value
+
+    def elapsed(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="flux-6144")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import resolution_diffusion_transformer_amd as A
+    import workloads as W
+
+    if not os.path.exists(A.library_path()):
+        from resolution_diffusion_transformer_amd import _build
+        _build.build(verbose=False)
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    A.lib()
+    dev = torch.device("cuda:0")
+    wl = W.get(args.workload)
+    p = A.problem_for(wl)
+    A.area_validate(p)
+    B, H, N, D = wl.B, wl.H, wl.N, wl.D
+    BH = B * H
+
+    log(f"[bench] generating {wl.name} inputs on the GPU")
+    q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
+    lat = torch.from_numpy(W.make_latent(wl)).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = max(A.area_workspace_bytes(p, op) for op in (A.OP_FULL, A.OP_COARSE, A.OP_PLAN, A.OP_WINDOW))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    plan = torch.zeros(A.area_plan_words(p), dtype=torch.int32, device=dev)
+    wsum = torch.empty(N, dtype=torch.int32, device=dev)
+    bridge = torch.empty((B, H, wl.bridge_k), dtype=torch.int32, device=dev)
+    energy = torch.empty((wl.Gh // 2, wl.Gw // 2), dtype=torch.float32, device=dev)
+    energy_q = torch.empty((wl.Gh // 2, wl.Gw // 2), dtype=torch.int32, device=dev)
+    n_steps = wl.p1_steps + wl.p2_steps
+    sched = [A.area_step_info(p, s) for s in range(n_steps)]
+    fs = sorted({st["f"] for st in sched if st["phase"] == A.PHASE_COARSE})
+    kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev),
+               torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev)) for f in fs}
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+
+    def tev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def one_pass(rec):
+        """Enqueue the whole hot path once; rec collects (kind, step, events)."""
+        for s, st in enumerate(sched):
+            if st["phase"] == A.PHASE_COARSE:
+                f = st["f"]
+                kp, vp = kpv[f]
+                e0 = tev()
+                A.area_pool_kv(p, f, k, v, kp, vp)
+                e1 = tev()
+                a0, a1 = ev.new(), ev.new()
+                A.area_set_attn_events(a0, a1)
+                A.area_coarse_attn(p, f, q, kp, vp, out, ws)
+                A.area_set_attn_events(None, None)
+                e2 = tev()
+                rec.append(("coarse", s, (e0, e1, e2, a0, a1)))
+            else:
+                e0 = tev()
+                A.area_dwt_detail(p, lat, energy, energy_q)
+                e1 = tev()
+                A.area_window_plan(p, s, energy_q, k, plan, wsum, bridge, ws)
+                e2 = tev()
+                a0, a1 = ev.new(), ev.new()
+                A.area_set_attn_events(a0, a1)
+                A.area_window_attn(p, s, plan, wsum, bridge, q, k, v, out, ws)
+                A.area_set_attn_events(None, None)
+                e3 = tev()
+                rec.append(("window", s, (e0, e1, e2, e3, a0, a1)))
+        e0 = tev()
+        a0, a1 = ev.new(), ev.new()
+        A.area_set_attn_events(a0, a1)
+        A.area_full_attn(p, q, k, v, out, ws)
+        A.area_set_attn_events(None, None)
+        e1 = tev()
+        rec.append(("full", -1, (e0, e1, a0, a1)))
+
+    # ---- algorithmic work per step (deterministic: plans depend only on the inputs)
+    log("[bench] counting algorithmic work")
+    flops = {}
+    win_pairs = {}
+    for s, st in enumerate(sched):
+        if st["phase"] == A.PHASE_COARSE:
+            flops[s] = 4.0 * D * BH * N * (N // (st["f"] ** 2))
+        else:
+            A.area_dwt_detail(p, lat, energy, energy_q)
+            A.area_window_plan(p, s, energy_q, k, plan, wsum, bridge, ws)
+            pl = plan.cpu().numpy()
+            br = bridge.cpu().numpy().reshape(BH, -1)
+            nwin = int(pl[0])
+            recs = pl[A.PLAN_HEADER:A.PLAN_HEADER + A.PLAN_REC * nwin].reshape(nwin, A.PLAN_REC)
+            by, bx = br // wl.Gw, br % wl.Gw
+            pairs = 0
+            for r in recs:
+                qy0, qx0, qh, qw, ky0, kx0, kh, kw = (int(x) for x in r[:8])
+                inside = (by >= ky0) & (by < ky0 + kh) & (bx >= kx0) & (bx < kx0 + kw)
+                nkv = kh * kw * BH + int((~inside).sum())
+                pairs += qh * qw * nkv
+            win_pairs[s] = pairs
+            flops[s] = 4.0 * D * pairs
+    full_flops = 4.0 * D * BH * float(N) * N
+
+    log(f"[bench] warmup x{args.warmup}")
+    for _ in range(args.warmup):
+        one_pass([])
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing x{args.steps}")
+    recs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_pass(recs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-phase times
+    agg = {k_: 0.0 for k_ in ("pool", "coarse_call", "coarse_kernel", "dwt", "plan", "window_call",
+                               "window_kernel", "full_call", "full_kernel")}
+    per_step = {}
+    for kind, s, e in recs:
+        if kind == "coarse":
+            e0, e1, e2, a0, a1 = e
+            t_pool, t_call, t_ker = e0.elapsed_time(e1), e1.elapsed_time(e2), ev.elapsed(a0, a1)
+            agg["pool"] += t_pool
+            agg["coarse_call"] += t_call
+            agg["coarse_kernel"] += t_ker
+            per_step.setdefault(s, []).append(t_pool + t_call)
+        elif kind == "window":
+            e0, e1, e2, e3, a0, a1 = e
+            t_dwt, t_plan, t_call, t_ker = e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3), ev.elapsed(a0, a1)
+            agg["dwt"] += t_dwt
+            agg["plan"] += t_plan
+            agg["window_call"] += t_call
+            agg["window_kernel"] += t_ker
+            per_step.setdefault(s, []).append(t_dwt + t_plan + t_call)
+        else:
+            e0, e1, a0, a1 = e
+            agg["full_call"] += e0.elapsed_time(e1)
+            agg["full_kernel"] += ev.elapsed(a0, a1)
+    K = args.steps
+    for k_ in agg:
+        agg[k_] /= K
+    area_ms = agg["pool"] + agg["coarse_call"] + agg["dwt"] + agg["plan"] + agg["window_call"]
+    area_ms_per_step = area_ms / n_steps
+    n_coarse = sum(1 for st in sched if st["phase"] == A.PHASE_COARSE)
+    n_win = n_steps - n_coarse
+    coarse_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_COARSE)
+    win_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_WINDOW)
+    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    win_tflops = tf(win_fl, agg["window_kernel"])
+    coarse_tflops = tf(coarse_fl, agg["coarse_kernel"])
+    full_ms = agg["full_call"]
+    full_tflops = tf(full_flops, agg["full_kernel"])
+    area_tflops = tf(coarse_fl + win_fl, area_ms)
+    # pooling bytes (mean mode): read K and V, write pooled K and V
+    pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 2
+                     for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
+    dwt_bytes = n_win * (wl.C * N * 4 + (N // 4) * 8)
+
+    # ---- CPU oracle baseline on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps)
+
+    phases = {
+        "pool_ms_per_call": agg["pool"] / max(n_coarse, 1),
+        "coarse_ms_per_call": agg["coarse_call"] / max(n_coarse, 1),
+        "coarse_kernel_tflops": coarse_tflops,
+        "dwt_ms_per_call": agg["dwt"] / max(n_win, 1),
+        "plan_ms_per_call": agg["plan"] / max(n_win, 1),
+        "window_ms_per_call": agg["window_call"] / max(n_win, 1),
+        "window_kernel_tflops": win_tflops,
+        "pool_gbs": pool_bytes / (agg["pool"] * 1e-3) / 1e9 if agg["pool"] > 0 else 0.0,
+        "dwt_gbs": dwt_bytes / (agg["dwt"] * 1e-3) / 1e9 if agg["dwt"] > 0 else 0.0,
+        "per_step_ms": [round(sum(per_step[s]) / len(per_step[s]), 3) for s in sorted(per_step)],
+        "schedule_tflop": (coarse_fl + win_fl) / 1e12,
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(area_ms_per_step, 4),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid": [wl.Gh, wl.Gw], "batch": B, "heads": H, "head_dim": D,
+                   "coarse_steps": n_coarse, "window_steps": n_win, "pool": "mean",
+                   "halo": wl.halo, "bridge_k": wl.bridge_k, "io": "bf16"},
+        "area_tflops": round(area_tflops, 2),
+        "area_pct_mfma_peak": round(100.0 * area_tflops / PEAK_MFMA_TFLOPS, 2),
+        "full_attn_ms": round(full_ms, 3),
+        "full_attn_tflops": round(full_tflops, 2),
+        "speedup_vs_full": round(full_ms / area_ms_per_step, 3),
+        "phases": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in phases.items()},
+        "roofline": {
+            "kernel": "attn_kernel (windowed)",
+            "bound": "mfma",
+            "achieved": round(win_tflops, 2),
+            "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(win_tflops / PEAK_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "launches_per_step": n_win,
+            "avg_launch_ms": round(agg["window_kernel"] / max(n_win, 1), 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
+    """The oracle on head 0 of two steps (first coarse step, last window
+    step), scaled by algorithmic work to the whole schedule and all heads."""
+    import numpy as np
+    import resolution_diffusion_transformer_amd as A
+    from oracle import area_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    log("[bench] cpu baseline: oracle on head 0 of the first coarse and the last window step")
+    qh = q[:, :1].float().cpu().numpy().astype(np.float64)
+    kh = k[:, :1].float().cpu().numpy().astype(np.float64)
+    vh = v[:, :1].float().cpu().numpy().astype(np.float64)
+    latn = lat.cpu().numpy()
+    s_c = next(s for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE)
+    s_w = max(s for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW)
+    f = sched[s_c]["f"]
+    t0 = time.perf_counter()
+    kp, vp = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, O.POOL_MEAN, wl.rope_theta)
+    O.coarse_attention(qh, kp, vp, wl.Gh, wl.Gw, f, wl.rope_theta)
+    t_c = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    t = s_w - wl.p1_steps
+    Eq = O.energy_fixed(O.detail_energy(latn))
+    plan = O.window_plan(wl.Gh, wl.Gw, sched[s_w]["w"], wl.halo, wl.seed, t, Eq)
+    br = O.bridge_select(kh[0, 0], wl.bridge_k, wl.Gh, wl.Gw)[None, None]
+    O.window_attention(qh, kh, vh, plan, br, wl.Gh, wl.Gw, wl.rope_theta)
+    t_w = time.perf_counter() - t0
+    H = wl.H * wl.B
+    # the sample is one head; flops[] ratios move it along the schedule, H scales it to all heads
+    coarse_total = H * sum(t_c * flops[s] / flops[s_c] for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE)
+    win_total = H * sum(t_w * flops[s] / flops[s_w] for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW)
+    ms_per_step = (coarse_total + win_total) * 1e3 / n_steps
+    return {"value": round(ms_per_step, 1), "unit": "ms/step", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle on head 0 of {H}: coarse step {s_c} (f={f}, all {wl.N} queries) "
+                       f"took {t_c:.2f} s, window step {s_w} (w={sched[s_w]['w']}, plan + bridge + "
+                       f"attention, all queries) took {t_w:.2f} s; scaled by algorithmic FLOPs to all "
+                       f"{n_steps} steps and {H} heads"),
+            "sample_seconds": round(t_c + t_w, 2)}
+
+
+if __name__ == "__main__":
+    main()

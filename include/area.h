@@ -155,6 +155,16 @@ size_t area_workspace_bytes(const area_problem* p, int op);
 /* int32 words of the plan buffer for any step of the problem. */
 size_t area_plan_words(const area_problem* p);
 
+/* Measurement hook for tracing (not needed for computing).  While set on
+ * the calling thread, every attention-kernel launch of a device call
+ * (area_full_attn, area_coarse_attn, area_window_attn) records the HIP event
+ * `ev_begin` just before the kernel and `ev_end` just after it, on the
+ * call's stream, so a profiler-free caller can time the MFMA kernel alone
+ * (without the operand preparation and blend kernels around it).  Events
+ * are hipEvent_t handles owned by the caller; pass NULL, NULL to clear.
+ * Thread-local; returns AREA_OK, or AREA_E_INVALID if exactly one is NULL. */
+int area_set_attn_events(void* ev_begin, void* ev_end);
+
 /* Human-readable text for a status, and the thread's last error detail. */
 const char* area_strerror(int status);
 const char* area_last_error(void);

@@ -18,7 +18,7 @@ __all__ = [
     "AreaError", "Problem", "lib", "library_path", "exported_symbols",
     "area_validate", "area_step_info", "area_f0", "area_base_windows", "area_workspace_bytes",
     "area_plan_words", "area_pool_kv", "area_coarse_attn", "area_dwt_detail",
-    "area_window_plan", "area_window_attn", "area_full_attn",
+    "area_window_plan", "area_window_attn", "area_full_attn", "area_set_attn_events",
     "POOL_MEAN", "POOL_CENTER", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
     "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "PLAN_HEADER", "PLAN_REC",
 ]
@@ -105,6 +105,7 @@ _SIGS = {
     "area_base_windows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]),
     "area_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int]),
     "area_plan_words": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "area_set_attn_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     "area_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "area_last_error": (ctypes.c_char_p, []),
     "area_pool_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
@@ -128,6 +129,10 @@ def lib():
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m resolution_diffusion_transformer_amd._build`")
+        try:  # let torch load its HIP runtime first so the process holds one copy
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)
@@ -186,6 +191,12 @@ def area_workspace_bytes(p: Problem, op: int) -> int:
 def area_plan_words(p: Problem) -> int:
     s, ref = _pp(p)
     return int(lib().area_plan_words(ref))
+
+
+def area_set_attn_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
+    """Record the given hipEvent_t handles around each attention kernel
+    launched by this thread (None, None to stop)."""
+    return _check(lib().area_set_attn_events(ev_begin, ev_end))
 
 
 # ----------------------------------------------------------- device calls --

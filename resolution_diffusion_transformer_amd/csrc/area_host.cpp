@@ -12,6 +12,9 @@
 namespace area {
 
 static thread_local std::string g_last_error;
+static thread_local AttnEvents g_attn_events;
+
+AttnEvents& attn_events() { return g_attn_events; }
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 
@@ -367,6 +370,14 @@ const char* area_strerror(int status) {
 }
 
 const char* area_last_error(void) { return g_last_error.c_str(); }
+
+int area_set_attn_events(void* ev_begin, void* ev_end) {
+  if ((ev_begin == nullptr) != (ev_end == nullptr))
+    return fail(AREA_E_INVALID, "pass both events or neither");
+  g_attn_events.begin = ev_begin;
+  g_attn_events.end = ev_end;
+  return AREA_OK;
+}
 
 int area_pool_kv(const area_problem* p, int f, const void* k, const void* v, void* kp, void* vp,
                  void* stream) {

@@ -17,7 +17,8 @@ int fail(int status, const std::string& msg);
 
 // ------------------------------------------------------- fixed constants --
 constexpr int kMaxAxisWindows = 64;    // base windows per axis (kernel-argument table)
-constexpr int kAttnBM = 256;           // queries per attention work item
+constexpr int kAttnQG = 1;             // 32-query groups per attention wave
+constexpr int kAttnBM = 128 * kAttnQG; // queries per attention work item (4 waves)
 constexpr int kAttnBN = 64;            // keys per staged tile
 constexpr int kBridgeChunk = 1024;     // rows per partial mean-key sum
 constexpr size_t kAlign = 256;
@@ -62,6 +63,13 @@ struct WindowStepInfo {
   int64_t max_items = 0;     // work items (window, query tile) over all split choices
 };
 int window_step(const area_problem& p, int step, WindowStepInfo& out);
+
+// Events recorded around attention-kernel launches (area_set_attn_events).
+struct AttnEvents {
+  void* begin = nullptr;
+  void* end = nullptr;
+};
+AttnEvents& attn_events();
 
 // ---------------------------------------------------------- launchers ----
 // Each returns AREA_OK or AREA_E_HIP (with the error text set).  Arguments

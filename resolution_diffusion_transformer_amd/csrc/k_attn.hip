@@ -35,6 +35,8 @@ namespace {
 
 typedef unsigned short u16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = kAttnBN;
@@ -98,22 +100,193 @@ __device__ inline int win_key(int s, const WinRect& r, int Gw, const int32_t* br
   return 0;
 }
 
-template <int D, int NW, int QG, bool WIN>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32 * QG;
-  constexpr int KD = D / 16;      // MFMA k-steps over the head dim (QK^T)
-  constexpr int DB = D / 32;      // 32-row blocks of O^T
-  constexpr int KS = D + 8;       // K tile row stride in LDS (bf16), breaks bank aliasing
-  constexpr int VS = BN + 8;      // V^T tile row stride in LDS
-  constexpr int CPR = D / 8;      // 16-byte chunks per token row
-  constexpr int K_CPT = BN * CPR / NT;
-  constexpr int VK = 8 * D / NT;  // keys per V^T store group
-  static_assert(K_CPT >= 1 && BN * CPR == K_CPT * NT, "K tile split");
-  static_assert(VK >= 1 && (BN / VK) * CPR == NT, "V tile split");
+// Per-thread staging of one 64-key tile: K rows as 16-byte chunks, V as
+// VK consecutive keys x 8 channels (written transposed to LDS).
+template <int D>
+struct TileRegs {
+  static constexpr int CPR = D / 8;
+  static constexpr int K_CPT = kAttnBN * CPR / 256;
+  static constexpr int VK = 8 * D / 256;
+  u32x4 k[K_CPT];
+  u32x4 v[VK];
+};
 
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * VS];
+template <bool WIN>
+__device__ __attribute__((always_inline)) inline int key_token(int s, int nkv, const WinRect& r, int Gw,
+                                                               const int32_t* br, int R, bool& valid) {
+  if constexpr (WIN) {
+    return win_key(s, r, Gw, br, R, valid);
+  } else {
+    valid = s < nkv;
+    return valid ? s : 0;
+  }
+}
+
+template <int D, bool WIN>
+__device__ __attribute__((always_inline)) inline void load_tile(TileRegs<D>& t, int tile, int tid, int nkv,
+                                                                const WinRect& r, int Gw, const int32_t* br, int R,
+                                                                const u16* kbase, const u16* vbase) {
+  constexpr int CPR = TileRegs<D>::CPR;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::K_CPT; ++i) {
+    int c = tid + i * 256;
+    int row = c / CPR, col = c - row * CPR;
+    bool ok;
+    int tok = key_token<WIN>(tile * kAttnBN + row, nkv, r, Gw, br, R, ok);
+    t.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)tok * D + col * 8);
+  }
+  int dc = tid % CPR, kg = tid / CPR;
+#pragma unroll
+  for (int q = 0; q < TileRegs<D>::VK; ++q) {
+    bool ok;
+    int tok = key_token<WIN>(tile * kAttnBN + kg * TileRegs<D>::VK + q, nkv, r, Gw, br, R, ok);
+    t.v[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)tok * D + dc * 8);
+  }
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_tile(const TileRegs<D>& t, u16* ks, u16* vt, int tid) {
+  constexpr int CPR = TileRegs<D>::CPR, VK = TileRegs<D>::VK;
+  constexpr int KS = D + 8, VS = kAttnBN + 8;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::K_CPT; ++i) {
+    int c = tid + i * 256;
+    int row = c / CPR, col = c - row * CPR;
+    *reinterpret_cast<u32x4*>(ks + row * KS + col * 8) = t.k[i];
+  }
+  int dc = tid % CPR, kg = tid / CPR;
+#pragma unroll
+  for (int jd = 0; jd < 8; ++jd) {
+    unsigned e[VK];
+#pragma unroll
+    for (int q = 0; q < VK; ++q) {
+      const unsigned w = t.v[q][jd >> 1];
+      e[q] = (jd & 1) ? (w >> 16) : (w & 0xFFFFu);
+    }
+    u16* dst = vt + (dc * 8 + jd) * VS + kg * VK;
+    if constexpr (VK == 4) {
+      u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+      *reinterpret_cast<u32x2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<unsigned*>(dst) = e[0] | (e[1] << 16);
+    }
+  }
+}
+
+// S^T (keys x queries) of one tile for the wave's QG groups of 32 queries.
+template <int D, int QG>
+__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG][2], const u16* ks, int krow_perm,
+                                                                  int hi, const f16x8 (&qf)[QG][D / 16]) {
+  constexpr int KS = D + 8;
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
+  const u16* kr = ks + krow_perm * KS + 8 * hi;
+#pragma unroll
+  for (int kd = 0; kd < D / 16; ++kd) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f16x8 af = *reinterpret_cast<const f16x8*>(kr + 32 * kb * KS + 16 * kd);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, qf[g][kd], s[g][kb], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T for one tile.
+template <int D, int QG>
+__device__ __attribute__((always_inline)) inline void tile_pv(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
+                                                              const f16x8 (&pf)[QG][4]) {
+  constexpr int VS = kAttnBN + 8;
+  const u16* vr = vt + n * VS + 8 * hi;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      f16x8 af = *reinterpret_cast<const f16x8*>(vr + 32 * db * VS + 16 * ks);
+#pragma unroll
+      for (int g = 0; g < QG; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[g][ks], o[g][db], 0, 0, 0);
+    }
+  }
+}
+
+// Keys of the tile that are not valid (tail of the key set, bridge tokens
+// already inside the Halo rectangle) get a -inf score.  vm holds one bit per
+// key of the tile; S^T register 8*jj + i of block kb is key
+// 32 kb + 16 jj + 8 hi + i.
+template <int QG>
+__device__ __attribute__((always_inline)) inline void mask_scores(f32x16 (&s)[QG][2], uint64_t vm, int hi) {
+  const uint32_t lm0 = (uint32_t)(vm >> (8 * hi));
+  const uint32_t lm1 = (uint32_t)(vm >> (32 + 8 * hi));
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t bits = kb ? lm1 : lm0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int bit = 16 * (i >> 3) + (i & 7);
+        s[g][kb][i] = ((bits >> bit) & 1u) ? s[g][kb][i] : -INFINITY;
+      }
+    }
+}
+
+// Online softmax of one tile (exp2 units, lazy maximum): P^T in fp16,
+// running sums updated, per-group rescale factors of O returned.
+template <int QG>
+__device__ __attribute__((always_inline)) inline void tile_softmax(const f32x16 (&s)[QG][2], float c,
+                                                                   float (&m_run)[QG], float (&l_run)[QG],
+                                                                   float (&alpha)[QG], f16x8 (&pf)[QG][4]) {
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    float mx = fmaxf(s[g][0][0], s[g][0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mc = mx * c;
+    const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
+    alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+    m_run[g] = m_new;
+    const float negm = -m_new;
+    float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f16x8 pv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][kb][8 * hh + i], c, negm));
+          if (i & 1) ls1 += p; else ls0 += p;
+          pv[i] = (_Float16)p;
+        }
+        pf[g][2 * kb + hh] = pv;
+      }
+    }
+    l_run[g] = l_run[g] * alpha[g] + (ls0 + ls1);
+  }
+}
+
+template <int D, bool WIN>
+__global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
+  constexpr int QG = kAttnQG;     // 32-query groups per wave
+  constexpr int BM = kAttnBM;     // 4 waves x QG groups x 32 queries
+  constexpr int KD = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int KS = D + 8;
+  constexpr int VS = BN + 8;
+  constexpr int K_ELEMS = BN * KS;
+  constexpr int V_ELEMS = D * VS;
+  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static_assert(BM == 4 * 32 * QG, "query tile");
+
+  // two LDS stages: the tile being multiplied and the tile being written
+  __shared__ __attribute__((aligned(16))) u16 smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -145,9 +318,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     nkv = a.Nk;
   }
   const int32_t* br = (WIN && a.R > 0) ? a.bridge + bh * a.R : nullptr;
-  const int64_t kv_rows = WIN ? 0 : (int64_t)a.Nk;
-  const u16* kbase = a.k + bh * (WIN ? (int64_t)a.Nq : kv_rows) * D;
-  const u16* vbase = a.v + bh * (WIN ? (int64_t)a.Nq : kv_rows) * D;
+  const int64_t kv_rows = WIN ? (int64_t)a.Nq : (int64_t)a.Nk;
+  const u16* kbase = a.k + bh * kv_rows * D;
+  const u16* vbase = a.v + bh * kv_rows * D;
   const u16* qbase = a.q + bh * (int64_t)a.Nq * D;
 
   // ---- queries of this lane
@@ -173,68 +346,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
     for (int kd = 0; kd < KD; ++kd) qf[g][kd] = qrow[2 * kd + hi];
   }
 
-  const int ntiles = (nkv + BN - 1) / BN;
+  const int nt = (nkv + BN - 1) / BN;
+  const float c = a.c;
+  const int krow_perm = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  // ---- global -> register prefetch of one K/V tile
-  uint4 kreg[K_CPT];
-  uint4 vreg[VK];
-  auto key_tok = [&](int s, bool& valid) -> int {
-    if constexpr (WIN) {
-      return win_key(s, r, a.Gw, br, a.R, valid);
-    } else {
-      valid = s < nkv;
-      return valid ? s : 0;
-    }
-  };
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < K_CPT; ++i) {
-      int c = tid + i * NT;
-      int row = c / CPR, col = c - row * CPR;
-      bool ok;
-      int tok = key_tok(j * BN + row, ok);
-      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)tok * D + col * 8);
-    }
-    {
-      int dc = tid % CPR, kg = tid / CPR;
-#pragma unroll
-      for (int q = 0; q < VK; ++q) {
-        bool ok;
-        int tok = key_tok(j * BN + kg * VK + q, ok);
-        vreg[q] = *reinterpret_cast<const uint4*>(vbase + (int64_t)tok * D + dc * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < K_CPT; ++i) {
-      int c = tid + i * NT;
-      int row = c / CPR, col = c - row * CPR;
-      *reinterpret_cast<uint4*>(&Ks[st][row * KS + col * 8]) = kreg[i];
-    }
-    int dc = tid % CPR, kg = tid / CPR;
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      u16 e[VK];
-#pragma unroll
-      for (int q = 0; q < VK; ++q) {
-        const unsigned w[4] = {vreg[q].x, vreg[q].y, vreg[q].z, vreg[q].w};
-        e[q] = (u16)((jd & 1) ? (w[jd >> 1] >> 16) : (w[jd >> 1] & 0xFFFFu));
-      }
-      u16* dst = &Vt[st][(dc * 8 + jd) * VS + kg * VK];
-      if constexpr (VK == 4) {
-        uint2 pk = make_uint2((unsigned)e[0] | ((unsigned)e[1] << 16), (unsigned)e[2] | ((unsigned)e[3] << 16));
-        *reinterpret_cast<uint2*>(dst) = pk;
-      } else if constexpr (VK == 2) {
-        *reinterpret_cast<unsigned*>(dst) = (unsigned)e[0] | ((unsigned)e[1] << 16);
-      } else {
-#pragma unroll
-        for (int q = 0; q < VK; ++q) dst[q] = e[q];
-      }
-    }
-  };
-
-  // ---- accumulators
   f32x16 o[QG][DB];
   float m_run[QG], l_run[QG];
 #pragma unroll
@@ -246,114 +361,46 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][db][i] = 0.0f;
   }
-  const float c = a.c;
-  // K row read by MFMA row n (swaps bits 2 and 3) so that S^T registers
-  // 8*jj + i of block kb hold key 32 kb + 16 jj + 8 hi + i.
-  const int krow_perm = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  load_tile(0);
-  store_tile(0);
+  // ---- prologue: tile 0 to LDS, tile 1 in flight
+  TileRegs<D> tr;
+  load_tile<D, WIN>(tr, 0, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
+  store_tile<D>(tr, smem, smem + K_ELEMS, tid);
+  load_tile<D, WIN>(tr, 1, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int st = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-
-    // validity of the tile's 64 keys (identical for every query)
+  for (int j = 0; j < nt; ++j) {
+    u16* ks = smem + (j & 1) * STAGE;
+    u16* vt = ks + K_ELEMS;
     uint64_t vm;
     {
       bool ok;
-      (void)key_tok(j * BN + lane, ok);
+      (void)key_token<WIN>(j * BN + lane, nkv, r, a.Gw, br, a.R, ok);
       vm = __ballot(ok);
     }
-    const bool full = (vm == ~0ull);
-    const uint32_t lm = (uint32_t)(vm >> (8 * hi)) & 0x00FF00FFu;   // bits 0..7, 16..23 used per block
-    const uint32_t lm_hi = (uint32_t)(vm >> (32 + 8 * hi)) & 0x00FF00FFu;
-
-    const u16* ks = Ks[st];
-    const u16* vt = Vt[st];
-
     f32x16 s[QG][2];
+    tile_scores<D, QG>(s, ks, krow_perm, hi, qf);
+    if (vm != ~0ull) mask_scores<QG>(s, vm, hi);
+    float alpha[QG];
+    f16x8 pf[QG][4];
+    tile_softmax<QG>(s, c, m_run, l_run, alpha, pf);
+    bool resc = false;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int g = 0; g < QG; ++g) resc |= alpha[g] != 1.0f;
+    if (__any(resc)) {
 #pragma unroll
       for (int g = 0; g < QG; ++g)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
-      const u16* kr = ks + (32 * kb + krow_perm) * KS + 8 * hi;
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd) {
-        f16x8 af = *reinterpret_cast<const f16x8*>(kr + 16 * kd);
-#pragma unroll
-        for (int g = 0; g < QG; ++g)
-          s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, qf[g][kd], s[g][kb], 0, 0, 0);
-      }
-    }
-
-    f16x8 pf[QG][4];
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint32_t bits = kb ? lm_hi : lm;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            int bit = 16 * (i >> 3) + (i & 7);
-            if (!((bits >> bit) & 1u)) s[g][kb][i] = -INFINITY;
-          }
-        }
-      }
-      float mx = s[g][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mc = mx * c;
-      const bool need = mc > m_run[g] + kLazy;
-      if (__any(need)) {
-        const float m_new = need ? mc : m_run[g];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-        l_run[g] *= alpha;
-#pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
-        m_run[g] = m_new;
-      }
-      const float negm = -m_run[g];
-      float ls = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          f16x8 pv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][kb][8 * hh + i], c, negm));
-            ls += p;
-            pv[i] = (_Float16)p;
-          }
-          pf[g][2 * kb + hh] = pv;
-        }
-      }
-      l_run[g] += ls;
+          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha[g];
     }
-
-#pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
-      const u16* vr = vt + n * VS + 16 * ks2 + 8 * hi;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        f16x8 af = *reinterpret_cast<const f16x8*>(vr + 32 * db * VS);
-#pragma unroll
-        for (int g = 0; g < QG; ++g)
-          o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[g][ks2], o[g][db], 0, 0, 0);
-      }
+    tile_pv<D, QG>(o, vt, n, hi, pf);
+    if (j + 1 < nt) {
+      u16* ks2 = smem + ((j + 1) & 1) * STAGE;
+      store_tile<D>(tr, ks2, ks2 + K_ELEMS, tid);
+      load_tile<D, WIN>(tr, j + 2, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
     }
-
-    if (j + 1 < ntiles) store_tile(st ^ 1);
     __syncthreads();
   }
 
@@ -554,18 +601,6 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* 
   }
 }
 
-// Kernel shape: waves per work-group and 32-query groups per wave (the
-// product times 32 is the query tile, 256).  AREA_ATTN_SHAPE=4x2 or 8x1
-// selects one for measurement; 4x2 is the default.
-int attn_shape() {
-  static int shape = [] {
-    const char* e = std::getenv("AREA_ATTN_SHAPE");
-    if (e && std::string(e) == "8x1") return 1;
-    return 0;
-  }();
-  return shape;
-}
-
 template <bool WIN>
 int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
   AttnArgs b = a;
@@ -573,18 +608,22 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
   if (g > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "attention grid too large");
   b.grid = (int)g;
   dim3 grid((unsigned)b.grid);
-  if (D == 128) {
-    if (attn_shape() == 1)
-      hipLaunchKernelGGL((attn_kernel<128, 8, 1, WIN>), grid, dim3(512), 0, st, b);
-    else
-      hipLaunchKernelGGL((attn_kernel<128, 4, 2, WIN>), grid, dim3(256), 0, st, b);
-  } else {
-    if (attn_shape() == 1)
-      hipLaunchKernelGGL((attn_kernel<64, 8, 1, WIN>), grid, dim3(512), 0, st, b);
-    else
-      hipLaunchKernelGGL((attn_kernel<64, 4, 2, WIN>), grid, dim3(256), 0, st, b);
+  AttnEvents ev = attn_events();
+  if (ev.begin) {
+    hipError_t e = hipEventRecord((hipEvent_t)ev.begin, st);
+    if (e != hipSuccess) return fail(AREA_E_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
   }
-  return check_launch(WIN ? "attn_kernel<window>" : "attn_kernel<dense>");
+  if (D == 128)
+    hipLaunchKernelGGL((attn_kernel<128, WIN>), grid, dim3(256), 0, st, b);
+  else
+    hipLaunchKernelGGL((attn_kernel<64, WIN>), grid, dim3(256), 0, st, b);
+  int rc = check_launch(WIN ? "attn_kernel<window>" : "attn_kernel<dense>");
+  if (rc) return rc;
+  if (ev.end) {
+    hipError_t e = hipEventRecord((hipEvent_t)ev.end, st);
+    if (e != hipSuccess) return fail(AREA_E_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
+  }
+  return AREA_OK;
 }
 
 }  // namespace
