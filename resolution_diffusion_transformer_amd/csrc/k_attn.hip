@@ -76,23 +76,43 @@ __device__ inline u16 f2bf(float f) {
   return (u16)(u >> 16);
 }
 
+// Unsigned division by a divisor d fixed per work item: q = umulhi(n, m)
+// with m = ceil(2^32 / d) is exact whenever n * d < 2^32 (key slots and
+// token indices here stay below 2^26 and d below 2^15); d = 1 is exact with
+// m = 0 handled by the caller's select.
+struct FastDiv {
+  unsigned m;
+  int d;
+  __device__ static FastDiv make(int d) {
+    FastDiv f;
+    f.d = d;
+    f.m = d > 1 ? 0xFFFFFFFFu / (unsigned)d + 1u : 0u;
+    return f;
+  }
+  __device__ __attribute__((always_inline)) int div(int n) const {
+    return d > 1 ? (int)__umulhi((unsigned)n, m) : n;
+  }
+};
+
 struct WinRect {
   int qy0, qx0, qh, qw, ky0, kx0, kh, kw;
+  FastDiv kwd, gwd;
 };
 
 // Token of key slot s of a window (Halo rectangle first, then the bridge
 // list); bridge tokens inside the rectangle are invalid (already present).
-__device__ inline int win_key(int s, const WinRect& r, int Gw, const int32_t* br, int R, bool& valid) {
+__device__ __attribute__((always_inline)) inline int win_key(int s, const WinRect& r, int Gw, const int32_t* br,
+                                                             int R, bool& valid) {
   int nrect = r.kh * r.kw;
   if (s < nrect) {
     valid = true;
-    int yy = s / r.kw;
+    int yy = r.kwd.div(s);
     return (r.ky0 + yy) * Gw + r.kx0 + (s - yy * r.kw);
   }
   int j = s - nrect;
   if (j < R) {
     int tok = br[j];
-    int y = tok / Gw, x = tok - (tok / Gw) * Gw;
+    int y = r.gwd.div(tok), x = tok - y * Gw;
     valid = !(y >= r.ky0 && y < r.ky0 + r.kh && x >= r.kx0 && x < r.kx0 + r.kw);
     return tok;
   }
@@ -118,7 +138,7 @@ __device__ __attribute__((always_inline)) inline int key_token(int s, int nkv, c
     return win_key(s, r, Gw, br, R, valid);
   } else {
     valid = s < nkv;
-    return valid ? s : 0;
+    return valid ? s : nkv - 1;
   }
 }
 
@@ -135,7 +155,8 @@ __device__ __attribute__((always_inline)) inline void load_tile(TileRegs<D>& t, 
     int tok = key_token<WIN>(tile * kAttnBN + row, nkv, r, Gw, br, R, ok);
     t.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)tok * D + col * 8);
   }
-  int dc = tid % CPR, kg = tid / CPR;
+  constexpr int KG = kAttnBN / TileRegs<D>::VK;  // key groups per tile
+  int kg = tid % KG, dc = tid / KG;
 #pragma unroll
   for (int q = 0; q < TileRegs<D>::VK; ++q) {
     bool ok;
@@ -152,9 +173,14 @@ __device__ __attribute__((always_inline)) inline void store_tile(const TileRegs<
   for (int i = 0; i < TileRegs<D>::K_CPT; ++i) {
     int c = tid + i * 256;
     int row = c / CPR, col = c - row * CPR;
-    *reinterpret_cast<u32x4*>(ks + row * KS + col * 8) = t.k[i];
+    // key row r lives in LDS row perm(r) (bits 2 and 3 swapped): MFMA row m
+    // then reads LDS row m, so the 8 lanes served together by a 128-bit
+    // read touch 8 consecutive rows, i.e. distinct banks
+    int prow = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
+    *reinterpret_cast<u32x4*>(ks + prow * KS + col * 8) = t.k[i];
   }
-  int dc = tid % CPR, kg = tid / CPR;
+  constexpr int KG = kAttnBN / VK;
+  int kg = tid % KG, dc = tid / KG;
 #pragma unroll
   for (int jd = 0; jd < 8; ++jd) {
     unsigned e[VK];
@@ -184,7 +210,7 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
-  const u16* kr = ks + krow_perm * KS + 8 * hi;
+  const u16* kr = ks + krow_perm * KS + 8 * hi;  // krow_perm: LDS row of MFMA row n
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
 #pragma unroll
@@ -234,6 +260,18 @@ __device__ __attribute__((always_inline)) inline void mask_scores(f32x16 (&s)[QG
     }
 }
 
+// Combine a value with the one held by the lane 32 apart (the other half of
+// the same query column), without a trip through LDS.
+__device__ __attribute__((always_inline)) inline float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __attribute__((always_inline)) inline float pair_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Online softmax of one tile (exp2 units, lazy maximum): P^T in fp16,
 // running sums updated, per-group rescale factors of O returned.
 template <int QG>
@@ -247,7 +285,7 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(const f32x16 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float mc = mx * c;
     const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
     alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
@@ -297,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
   const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
   int64_t bh;
   int qtile = 0, rec = 0;
-  WinRect r = {0, 0, 0, 0, 0, 0, 0, 0};
+  WinRect r = {};
   int nq, nkv;
   if constexpr (WIN) {
     bh = L / a.max_items;
@@ -308,6 +346,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
     const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
     r.qy0 = rp[0]; r.qx0 = rp[1]; r.qh = rp[2]; r.qw = rp[3];
     r.ky0 = rp[4]; r.kx0 = rp[5]; r.kh = rp[6]; r.kw = rp[7];
+    r.kwd = FastDiv::make(r.kw);
+    r.gwd = FastDiv::make(a.Gw);
     nq = r.qh * r.qw;
     nkv = r.kh * r.kw + a.R;
   } else {
@@ -348,7 +388,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
 
   const int nt = (nkv + BN - 1) / BN;
   const float c = a.c;
-  const int krow_perm = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+  // MFMA row n of the score tile is key perm(n) (bits 2 and 3 swapped), so
+  // that S^T registers 8*jj + i of block kb hold key 32 kb + 16 jj + 8 hi + i;
+  // store_tile already placed key perm(n) in LDS row n.
+  const int krow_perm = n;
 
   f32x16 o[QG][DB];
   float m_run[QG], l_run[QG];
@@ -407,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
   // ---- epilogue: normalise and write
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    float lt = l_run[g] + __shfl_xor(l_run[g], 32);
+    float lt = pair_sum(l_run[g]);
     float inv = 1.0f / lt;
     if (!qvalid[g]) continue;
     if constexpr (WIN) {
