@@ -176,6 +176,14 @@ int window_step(const area_problem& p, int step, WindowStepInfo& out) {
   int64_t split = ceil_div(h1 * w1, kAttnBM) + ceil_div(h1 * (Lx - w1), kAttnBM) +
                   ceil_div((Ly - h1) * w1, kAttnBM) + ceil_div((Ly - h1) * (Lx - w1), kAttnBM);
   out.max_items = nb * (unsplit > split ? unsplit : split);
+  // gathered key tiles: Halo rectangle (clipped to the grid) + all R bridge
+  // slots per window, rounded up to 64 keys
+  int64_t R = p.bridge_k;
+  int64_t kh = std::min<int64_t>(Ly + 2 * p.halo, p.Gh), kw = std::min<int64_t>(Lx + 2 * p.halo, p.Gw);
+  int64_t qh = std::min<int64_t>(Ly - h1 + 2 * p.halo, p.Gh), qw = std::min<int64_t>(Lx - w1 + 2 * p.halo, p.Gw);
+  int64_t g_unsplit = ceil_div(kh * kw + R, kAttnBN);
+  int64_t g_split = 4 * ceil_div(qh * qw + R, kAttnBN);
+  out.max_gtiles = nb * (g_unsplit > g_split ? g_unsplit : g_split);
   return AREA_OK;
 }
 
@@ -228,7 +236,7 @@ static int64_t N_of(const area_problem& p) { return (int64_t)p.Gh * p.Gw; }
 static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * N_of(p) * p.D * 2; }
 
 struct WindowMax {
-  int64_t q_total = 0, max_items = 0;
+  int64_t q_total = 0, max_items = 0, max_gtiles = 0;
   int max_windows = 0, n_base = 0;
 };
 
@@ -240,18 +248,46 @@ static WindowMax window_max(const area_problem& p) {
     int nb = wi.ty.n * wi.tx.n;
     m.q_total = std::max<int64_t>(m.q_total, wi.q_total);
     m.max_items = std::max<int64_t>(m.max_items, wi.max_items);
+    m.max_gtiles = std::max<int64_t>(m.max_gtiles, wi.max_gtiles);
     m.max_windows = std::max(m.max_windows, 4 * nb);
     m.n_base = std::max(m.n_base, nb);
   }
   return m;
 }
 
+// Regions of the windowed-attention workspace, in order.
+struct WindowLayout {
+  size_t q, k, slots, items, kg, vg, blist, bcount, total;
+};
+
+static WindowLayout window_layout(const area_problem& p) {
+  WindowMax m = window_max(p);
+  int64_t BH = BH_of(p);
+  WindowLayout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  l.q = take(tok_bytes(p));
+  l.k = take(tok_bytes(p));
+  l.slots = take((size_t)m.q_total * BH * p.D * 4);
+  l.items = take(window_items_ws_bytes(m.max_windows, m.max_items, m.n_base, m.max_gtiles));
+  l.kg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
+  l.vg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
+  l.blist = take((size_t)m.max_windows * BH * std::max(p.bridge_k, 1) * 4);
+  l.bcount = take((size_t)m.max_windows * BH * 4);
+  l.total = off;
+  return l;
+}
+
 static size_t workspace_bytes(const area_problem& p, int op) {
   switch (op) {
     case AREA_OP_FULL:
-      return 3 * align_up(tok_bytes(p));
+      return 2 * align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)N_of(p), p.D));
     case AREA_OP_COARSE:
-      return align_up(tok_bytes(p));
+      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)N_of(p), p.D));
     case AREA_OP_PLAN: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
       WindowMax m = window_max(p);
@@ -260,9 +296,7 @@ static size_t workspace_bytes(const area_problem& p, int op) {
     }
     case AREA_OP_WINDOW: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
-      WindowMax m = window_max(p);
-      return 3 * align_up(tok_bytes(p)) + align_up((size_t)m.q_total * BH_of(p) * p.D * 4) +
-             align_up(window_items_ws_bytes(m.max_windows, m.max_items, m.n_base));
+      return window_layout(p).total;
     }
     default:
       return 0;
@@ -399,10 +433,14 @@ int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp
   int64_t BH = BH_of(*p);
   int N = (int)N_of(*p);
   int M = N / (f * f);
-  rc = launch_prep(q, nullptr, nullptr, ws, nullptr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
+  char* qr = (char*)ws;
+  char* vt = qr + align_up(tok_bytes(*p));
+  rc = launch_prep(q, nullptr, nullptr, qr, nullptr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
                    stream);
   if (rc) return rc;
-  return launch_dense_attn(ws, kp, vp, out, BH, N, M, p->D, stream);
+  rc = launch_vt(vp, vt, BH, M, p->D, false, stream);
+  if (rc) return rc;
+  return launch_dense_attn(qr, kp, vt, out, BH, N, M, p->D, stream);
 }
 
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out,
@@ -416,10 +454,12 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
   int N = (int)N_of(*p);
   char* qr = (char*)ws;
   char* kr = qr + align_up(tok_bytes(*p));
-  char* vr = kr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, k, v, qr, kr, vr, BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  char* vt = kr + align_up(tok_bytes(*p));
+  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kr, vr, out, BH, N, N, p->D, stream);
+  rc = launch_vt(v, vt, BH, N, p->D, true, stream);
+  if (rc) return rc;
+  return launch_dense_attn(qr, kr, vt, out, BH, N, N, p->D, stream);
 }
 
 int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
@@ -486,7 +526,6 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   if (!plan || !wsum || !q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
   rc = check_ws(*p, AREA_OP_WINDOW, ws, ws_bytes);
   if (rc) return rc;
-  WindowMax m = window_max(*p);
   WindowAttnArgs a;
   std::memset(&a, 0, sizeof(a));
   a.Gh = p->Gh;
@@ -496,21 +535,26 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   a.BH = BH_of(*p);
   a.max_windows = 4 * wi.ty.n * wi.tx.n;
   a.max_items = wi.max_items;
+  a.max_gtiles = wi.max_gtiles;
   a.ny = wi.ty.n;
   a.nx = wi.tx.n;
   a.Ly = wi.ty.L;
   a.Lx = wi.tx.L;
   for (int i = 0; i < a.ny; ++i) a.ys[i] = wi.ty.start[i];
   for (int i = 0; i < a.nx; ++i) a.xs[i] = wi.tx.start[i];
-  char* qr = (char*)ws;
-  char* kr = qr + align_up(tok_bytes(*p));
-  char* vr = kr + align_up(tok_bytes(*p));
-  float* slots = (float*)(vr + align_up(tok_bytes(*p)));
-  char* items = (char*)slots + align_up((size_t)m.q_total * BH_of(*p) * p->D * 4);
-  rc = launch_prep(q, k, v, qr, kr, vr, a.BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  WindowLayout l = window_layout(*p);
+  char* base = (char*)ws;
+  WindowWs w;
+  w.items = base + l.items;
+  w.slots = (float*)(base + l.slots);
+  w.kg = base + l.kg;
+  w.vg = base + l.vg;
+  w.blist = (int*)(base + l.blist);
+  w.bcount = (int*)(base + l.bcount);
+  rc = launch_prep(q, k, nullptr, base + l.q, base + l.k, nullptr, a.BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
+                   stream);
   if (rc) return rc;
-  return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, qr, kr, vr, out, items, slots,
-                            stream);
+  return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, base + l.q, base + l.k, v, out, w, stream);
 }
 
 }  // extern "C"

@@ -61,6 +61,7 @@ struct WindowStepInfo {
   AxisTiling ty, tx;
   int64_t q_total = 0;       // sum of query areas (== with splits)
   int64_t max_items = 0;     // work items (window, query tile) over all split choices
+  int64_t max_gtiles = 0;    // gathered 64-key tiles over all split choices
 };
 int window_step(const area_problem& p, int step, WindowStepInfo& out);
 
@@ -99,22 +100,37 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D
                   int rw, void* ws, stream_t s);
 size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
 
-// Attention over fp16 operands (rotated q and k, v), bf16 output.
-int launch_dense_attn(const void* q_rot, const void* k_rot, const void* v, void* out, int64_t BH,
+// fp16 V^T tiles of 64 keys: vt[bh][t][d][k] = v[bh][64 t + k][d], zero
+// padded; v is bf16 (bf16_in) or fp16.
+size_t vt_bytes(int64_t BH, int M, int D);
+int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, stream_t s);
+
+// Attention over fp16 operands (rotated q, rotated k rows, V^T tiles), bf16
+// output.
+int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH,
                       int Nq, int Nk, int D, stream_t s);
 
 struct WindowAttnArgs {
   int Gh, Gw, D, R;
   int64_t BH;
   int max_windows;
-  int64_t max_items;
+  int64_t max_items, max_gtiles;
   int ny, nx;
   int ys[kMaxAxisWindows], xs[kMaxAxisWindows];
   int Ly, Lx;
 };
+// Workspace regions of the windowed attention.
+struct WindowWs {
+  void* items;     // window_items_ws_bytes
+  float* slots;    // [q_total][BH][D] fp32
+  void* kg;        // [BH][max_gtiles * 64][D] fp16 gathered keys
+  void* vg;        // [BH][max_gtiles][D][64] fp16 gathered V^T tiles
+  int* blist;      // [max_windows][BH][R] kept bridge tokens
+  int* bcount;     // [max_windows][BH]
+};
 int launch_window_attn(const WindowAttnArgs& a, const int32_t* plan, const int32_t* wsum,
                        const int32_t* bridge_idx, const void* q_rot, const void* k_rot,
-                       const void* v, void* out, void* items_ws, float* slots, stream_t s);
-size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base);
+                       const void* v, void* out, const WindowWs& ws, stream_t s);
+size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base, int64_t max_gtiles);
 
 }  // namespace area

@@ -1,24 +1,29 @@
-// Flash-style attention on gfx950 for the AReA path: dense (full attention,
-// Phase I coarse attention over pooled keys) and windowed (Phase II: Halo
-// rectangle + bridge keys, tent-weighted blending of overlaps).
+// Flash-style attention on gfx950 for the AReA path: full attention, Phase I
+// coarse attention over pooled keys, and Phase II windowed attention (Halo
+// rectangle + global-KV bridge, tent-weighted blending of overlaps).
 //
 // Design (CDNA4, wave64):
-//  * MFMA v_mfma_f32_32x32x16_f16 with fp32 accumulation for both Q K^T and
-//    P V.  The operands (rotated Q and K, V, P) are IEEE fp16: the same MFMA
-//    rate as bf16 with three more mantissa bits, so the bf16 rounding of the
-//    output is the only coarse rounding on the path.
-//  * The score tile is computed transposed, S^T = K Q^T, so that each lane
-//    owns one query column: the softmax max/sum over keys is an in-lane
-//    reduction plus one exchange with the partner lane (lane ^ 32).
-//  * K rows are read in a permuted order so that the S^T accumulator
-//    registers already form the bf16 B operand of O^T += V^T P^T; P never
-//    leaves registers.
-//  * K (row-major) and V (transposed) tiles of 64 keys are staged through
-//    LDS, double-buffered, with the next tile's global loads in flight while
-//    the current tile is computed; one barrier per tile.
+//  * One attention kernel for every mode.  Its key/value set is always a
+//    contiguous run of fp16 K rows plus fp16 V^T tiles of 64 keys: full and
+//    coarse attention use the prepared tensors directly, windowed attention
+//    first gathers each window's keys (Halo rectangle, then the bridge tokens
+//    outside it, compacted) with a bandwidth-bound kernel, so no index math or
+//    transposition remains in the MFMA loop.
+//  * MFMA v_mfma_f32_32x32x16_f16 with fp32 accumulation for Q K^T and P V.
+//    fp16 operands run at the bf16 rate with three more mantissa bits, so the
+//    bf16 rounding of the output is the only coarse rounding on the path.
+//  * Scores are computed transposed, S^T = K Q^T: each lane owns one query
+//    column, the softmax max/sum over keys is an in-lane reduction plus one
+//    v_permlane32_swap with the partner lane.  K rows sit in LDS in the
+//    order that makes the S^T accumulator registers the fp16 B operand of
+//    O^T += V^T P^T, so P never leaves registers.
+//  * K and V^T tiles are staged through LDS (double-buffered, padded rows,
+//    conflict-free 128-bit accesses) with the next tile's global loads in
+//    flight; one barrier per tile.  Four waves of 32 queries use ~220 VGPRs,
+//    so two work-groups share a CU and overlap each other's softmax (VALU)
+//    and MFMA phases.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
-//    only moves when a new score exceeds it by more than 2^8, so the O
-//    rescale is skipped on almost every tile.
+//    only moves when a score exceeds it by more than 2^8.
 //  * Work items are mapped XCD-aware: consecutive items (same head, same
 //    window) land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -36,7 +41,6 @@ namespace {
 typedef unsigned short u16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = kAttnBN;
@@ -48,129 +52,296 @@ int check_launch(const char* what) {
   return AREA_OK;
 }
 
-struct AttnArgs {
-  const u16* q;        // rotated queries, fp16 [BH][Nq][D]
-  const u16* k;        // rotated keys, fp16 [BH][Nk][D]   (window mode: [BH][N][D])
-  const u16* v;        // values, fp16 [BH][Nk][D]
-  u16* out;            // [BH][Nq][D]
-  int64_t BH;
-  int Nq, Nk;          // dense mode sizes
-  int n_qtiles;        // dense mode: query tiles per head
-  int grid;            // launched work-groups (multiple of 8)
-  float c;             // log2(e) / sqrt(D)
-  // window mode
-  const int32_t* plan;
-  const int32_t* wsum;
-  const int32_t* bridge;   // [BH][R] or null
-  const int* items;        // [max_items][2] = (record, query tile)
-  const int* n_items;
-  const int* slot_off;     // per record: first slot of its query rect
-  float* slots;            // [slot][BH][D] fp32 outputs of overlapped tokens
-  int Gw, R;
-  int64_t max_items;
-};
-
 __device__ inline u16 f2bf(float f) {
   unsigned u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (u16)(u >> 16);
 }
 
-// Unsigned division by a divisor d fixed per work item: q = umulhi(n, m)
-// with m = ceil(2^32 / d) is exact whenever n * d < 2^32 (key slots and
-// token indices here stay below 2^26 and d below 2^15); d = 1 is exact with
-// m = 0 handled by the caller's select.
-struct FastDiv {
-  unsigned m;
-  int d;
-  __device__ static FastDiv make(int d) {
-    FastDiv f;
-    f.d = d;
-    f.m = d > 1 ? 0xFFFFFFFFu / (unsigned)d + 1u : 0u;
-    return f;
-  }
-  __device__ __attribute__((always_inline)) int div(int n) const {
-    return d > 1 ? (int)__umulhi((unsigned)n, m) : n;
-  }
-};
-
-struct WinRect {
-  int qy0, qx0, qh, qw, ky0, kx0, kh, kw;
-  FastDiv kwd, gwd;
-};
-
-// Token of key slot s of a window (Halo rectangle first, then the bridge
-// list); bridge tokens inside the rectangle are invalid (already present).
-__device__ __attribute__((always_inline)) inline int win_key(int s, const WinRect& r, int Gw, const int32_t* br,
-                                                             int R, bool& valid) {
-  int nrect = r.kh * r.kw;
-  if (s < nrect) {
-    valid = true;
-    int yy = r.kwd.div(s);
-    return (r.ky0 + yy) * Gw + r.kx0 + (s - yy * r.kw);
-  }
-  int j = s - nrect;
-  if (j < R) {
-    int tok = br[j];
-    int y = r.gwd.div(tok), x = tok - y * Gw;
-    valid = !(y >= r.ky0 && y < r.ky0 + r.kh && x >= r.kx0 && x < r.kx0 + r.kw);
-    return tok;
-  }
-  valid = false;
-  return 0;
+__device__ inline u16 bf_to_f16(u16 b) {
+  _Float16 h = (_Float16)__uint_as_float(((unsigned)b) << 16);
+  return __builtin_bit_cast(u16, h);
 }
 
-// Per-thread staging of one 64-key tile: K rows as 16-byte chunks, V as
-// VK consecutive keys x 8 channels (written transposed to LDS).
+// ------------------------------------------------------------ V^T tiles --
+// out[bh][t][d][k] = in[bh][64 t + k][d] as fp16, zero for rows >= M.
+template <int D, bool IN_BF16>
+__global__ __launch_bounds__(256) void vt_kernel(const u16* __restrict__ in, u16* __restrict__ out, int M,
+                                                 int tiles) {
+  constexpr int CPR = D / 8;
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
+  const int t = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const u16* src = in + bh * (int64_t)M * D;
+  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
+    int row = c / CPR, col = c - row * CPR;
+    int key = t * BN + row;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (key < M) {
+      v = *reinterpret_cast<const u32x4*>(src + (int64_t)key * D + col * 8);
+      if constexpr (IN_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = (unsigned)bf_to_f16((u16)(v[i] & 0xFFFFu)) | ((unsigned)bf_to_f16((u16)(v[i] >> 16)) << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = v;
+  }
+  __syncthreads();
+  u16* dst = out + (bh * tiles + t) * (int64_t)D * BN;
+  for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
+    int d = c / (BN / 8), k8 = c - d * (BN / 8);
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (unsigned)buf[(8 * k8 + 2 * i) * LS + d] | ((unsigned)buf[(8 * k8 + 2 * i + 1) * LS + d] << 16);
+    *reinterpret_cast<u32x4*>(dst + d * BN + 8 * k8) = v;
+  }
+}
+
+// ------------------------------------------------- window work structures --
+// Items workspace: counters, per-record slot / key-tile offsets, the first
+// record of every base window, the (record, query tile) list and the
+// (record, key tile) list of the gather.
+struct ItemsWs {
+  int* n_items;       // [0] attention items, [1] gather tiles
+  int* slot_off;      // [max_windows] first fp32 output slot of a record
+  int* kv_tile_off;   // [max_windows] first gathered key tile of a record
+  int* rec_start;     // [n_base]
+  int* items;         // [max_items][2]
+  int* gtiles;        // [max_gtiles][2]
+};
+
+ItemsWs make_items_ws(void* ws, int max_windows, int n_base, int64_t max_items) {
+  ItemsWs w;
+  char* p = (char*)ws;
+  w.n_items = (int*)p;
+  p += align_up(2 * sizeof(int));
+  w.slot_off = (int*)p;
+  p += align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1));
+  w.kv_tile_off = (int*)p;
+  p += align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1));
+  w.rec_start = (int*)p;
+  p += align_up(sizeof(int) * (n_base > 0 ? n_base : 1));
+  w.items = (int*)p;
+  p += align_up(sizeof(int) * 2 * (max_items > 0 ? max_items : 1));
+  w.gtiles = (int*)p;
+  return w;
+}
+
+// One block: slot offsets (prefix of query areas in record order), key-tile
+// offsets (prefix of ceil((kh kw + R) / 64)), the first record of every base
+// window, the (record, query tile) list -- whole windows first, quadrants
+// after (largest key sets first) -- and the (record, key tile) list.
+__global__ __launch_bounds__(256) void items_kernel(const int32_t* __restrict__ plan, ItemsWs w, int BM, int R,
+                                                    int max_windows, int64_t max_items, int64_t max_gtiles) {
+  __shared__ int s_item_off[4 * kMaxAxisWindows * kMaxAxisWindows];
+  int nwin = plan[AREA_PH_NWIN];
+  if (nwin > max_windows) nwin = max_windows;
+  if (threadIdx.x == 0) {
+    int it = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int i = 0; i < nwin; ++i) {
+        const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+        bool quad = rp[9] >= 0;
+        if ((pass == 0) == quad) continue;
+        s_item_off[i] = it;
+        it += (rp[2] * rp[3] + BM - 1) / BM;
+      }
+    }
+    int qs = 0, kt = 0;
+    for (int i = 0; i < nwin; ++i) {
+      const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+      w.slot_off[i] = qs;
+      qs += rp[2] * rp[3];
+      w.kv_tile_off[i] = kt;
+      kt += (rp[6] * rp[7] + R + BN - 1) / BN;
+      if (rp[9] <= 0) w.rec_start[rp[8]] = i;
+    }
+    w.n_items[0] = it < max_items ? it : (int)max_items;
+    w.n_items[1] = kt < max_gtiles ? kt : (int)max_gtiles;
+  }
+  __syncthreads();
+  for (int i = 0; i < nwin; ++i) {
+    const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
+    int nt = (rp[2] * rp[3] + BM - 1) / BM;
+    for (int t = threadIdx.x; t < nt; t += blockDim.x) {
+      int idx = s_item_off[i] + t;
+      if (idx < max_items) {
+        w.items[2 * idx] = i;
+        w.items[2 * idx + 1] = t;
+      }
+    }
+    int kt = (rp[6] * rp[7] + R + BN - 1) / BN;
+    for (int t = threadIdx.x; t < kt; t += blockDim.x) {
+      int idx = w.kv_tile_off[i] + t;
+      if (idx < max_gtiles) {
+        w.gtiles[2 * idx] = i;
+        w.gtiles[2 * idx + 1] = t;
+      }
+    }
+  }
+}
+
+// Bridge tokens outside each window's Halo rectangle, in ascending order:
+// list[(rec * BH + bh) * R + i], count[rec * BH + bh].  One block per
+// (record, batch*head).
+__global__ __launch_bounds__(256) void bridge_compact_kernel(const int32_t* __restrict__ plan,
+                                                             const int32_t* __restrict__ bridge, int* __restrict__ list,
+                                                             int* __restrict__ count, int R, int Gw, int64_t BH) {
+  __shared__ int s_wave[4];
+  const int rec = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (rec >= plan[AREA_PH_NWIN]) return;
+  const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
+  const int ky0 = rp[4], kx0 = rp[5], kh = rp[6], kw = rp[7];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int* dst = list + ((int64_t)rec * BH + bh) * R;
+  int base = 0;
+  for (int j0 = 0; j0 < R; j0 += 256) {
+    int j = j0 + threadIdx.x;
+    int tok = 0;
+    bool keep = false;
+    if (j < R) {
+      tok = bridge[bh * R + j];
+      int y = tok / Gw, x = tok - y * Gw;
+      keep = !(y >= ky0 && y < ky0 + kh && x >= kx0 && x < kx0 + kw);
+    }
+    uint64_t m = __ballot(keep);
+    int before = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+    if (lane == 0) s_wave[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int i = 0; i < wave; ++i) off += s_wave[i];
+    if (keep) dst[off + before] = tok;
+    int tot = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    __syncthreads();
+    base += tot;
+  }
+  if (threadIdx.x == 0) count[(int64_t)rec * BH + bh] = base;
+}
+
+// Gathers one 64-key tile of a window's key set: slot s < kh*kw is the Halo
+// rectangle token s (row-major), then the compacted outside bridge tokens,
+// then zero rows.  K rows are copied (already rotated, fp16); V rows are
+// converted bf16 -> fp16 and written transposed.
+template <int D>
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan, const int* __restrict__ gtiles,
+                                                     const int* __restrict__ n_items, const int* __restrict__ kv_tile_off,
+                                                     const int* __restrict__ list, const int* __restrict__ count,
+                                                     const u16* __restrict__ kr, const u16* __restrict__ v,
+                                                     u16* __restrict__ kg, u16* __restrict__ vg, int64_t cap_tiles,
+                                                     int R, int Gw, int N, int64_t BH) {
+  constexpr int CPR = D / 8;
+  constexpr int LS = D + 8;
+  __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
+  __shared__ int s_tok[BN];
+  const int g = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (g >= n_items[1]) return;
+  const int rec = gtiles[2 * g], t = gtiles[2 * g + 1];
+  const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
+  const int ky0 = rp[4], kx0 = rp[5], kw = rp[7];
+  const int nrect = rp[6] * kw;
+  const int cnt = R > 0 ? count[(int64_t)rec * BH + bh] : 0;
+  const int T = kv_tile_off[rec] + t;
+  if (threadIdx.x < BN) {
+    int s = t * BN + threadIdx.x;
+    int tok = -1;
+    if (s < nrect) {
+      int yy = s / kw;
+      tok = (ky0 + yy) * Gw + kx0 + (s - yy * kw);
+    } else if (s - nrect < cnt) {
+      tok = list[((int64_t)rec * BH + bh) * R + (s - nrect)];
+    }
+    s_tok[threadIdx.x] = tok;
+  }
+  __syncthreads();
+  const u16* ksrc = kr + bh * (int64_t)N * D;
+  const u16* vsrc = v + bh * (int64_t)N * D;
+  u16* kdst = kg + (bh * cap_tiles + T) * (int64_t)BN * D;
+  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
+    int row = c / CPR, col = c - row * CPR;
+    int tok = s_tok[row];
+    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (tok >= 0) {
+      kv = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)tok * D + col * 8);
+      vv = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)tok * D + col * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vv[i] = (unsigned)bf_to_f16((u16)(vv[i] & 0xFFFFu)) | ((unsigned)bf_to_f16((u16)(vv[i] >> 16)) << 16);
+    }
+    *reinterpret_cast<u32x4*>(kdst + row * D + col * 8) = kv;
+    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = vv;
+  }
+  __syncthreads();
+  u16* vdst = vg + (bh * cap_tiles + T) * (int64_t)D * BN;
+  for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
+    int d = c / (BN / 8), k8 = c - d * (BN / 8);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (unsigned)buf[(8 * k8 + 2 * i) * LS + d] | ((unsigned)buf[(8 * k8 + 2 * i + 1) * LS + d] << 16);
+    *reinterpret_cast<u32x4*>(vdst + d * BN + 8 * k8) = o;
+  }
+}
+
+// -------------------------------------------------------------- attention --
+struct AttnArgs {
+  const u16* q;        // rotated queries, fp16 [BH][Nq][D]
+  const u16* k;        // fp16 key rows [BH][k_rows][D]
+  const u16* vt;       // fp16 V^T tiles [BH][k_tiles][D][64]
+  u16* out;            // bf16 [BH][Nq][D]
+  int64_t BH;
+  int Nq;
+  int64_t k_rows, k_tiles;  // per-(batch*head) strides of k and vt
+  int n_kv;            // dense mode: keys per query
+  int n_qtiles;        // dense mode: query tiles per head
+  int grid;            // launched work-groups (multiple of 8)
+  float c;             // log2(e) / sqrt(D)
+  // window mode
+  const int32_t* plan;
+  const int32_t* wsum;
+  const int* items;        // [max_items][2] = (record, query tile)
+  const int* n_items;
+  const int* slot_off;     // per record: first fp32 output slot
+  const int* kv_tile_off;  // per record: first gathered key tile
+  const int* bcount;       // [record][BH] bridge tokens kept
+  float* slots;            // [slot][BH][D] fp32 outputs of overlapped tokens
+  int Gw, R;
+  int64_t max_items;
+};
+
+// Per-thread staging of one 64-key tile: 16-byte chunks of K rows and of the
+// V^T tile.
 template <int D>
 struct TileRegs {
-  static constexpr int CPR = D / 8;
-  static constexpr int K_CPT = kAttnBN * CPR / 256;
-  static constexpr int VK = 8 * D / 256;
-  u32x4 k[K_CPT];
-  u32x4 v[VK];
+  static constexpr int CH = BN * D / 8 / 256;  // chunks per thread (4 at D=128)
+  u32x4 k[CH];
+  u32x4 v[CH];
 };
 
-template <bool WIN>
-__device__ __attribute__((always_inline)) inline int key_token(int s, int nkv, const WinRect& r, int Gw,
-                                                               const int32_t* br, int R, bool& valid) {
-  if constexpr (WIN) {
-    return win_key(s, r, Gw, br, R, valid);
-  } else {
-    valid = s < nkv;
-    return valid ? s : nkv - 1;
-  }
-}
-
-template <int D, bool WIN>
+template <int D>
 __device__ __attribute__((always_inline)) inline void load_tile(TileRegs<D>& t, int tile, int tid, int nkv,
-                                                                const WinRect& r, int Gw, const int32_t* br, int R,
-                                                                const u16* kbase, const u16* vbase) {
-  constexpr int CPR = TileRegs<D>::CPR;
+                                                                const u16* kbase, const u16* vtbase) {
+  constexpr int CPR = D / 8;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::K_CPT; ++i) {
+  for (int i = 0; i < TileRegs<D>::CH; ++i) {
     int c = tid + i * 256;
     int row = c / CPR, col = c - row * CPR;
-    bool ok;
-    int tok = key_token<WIN>(tile * kAttnBN + row, nkv, r, Gw, br, R, ok);
-    t.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)tok * D + col * 8);
-  }
-  constexpr int KG = kAttnBN / TileRegs<D>::VK;  // key groups per tile
-  int kg = tid % KG, dc = tid / KG;
-#pragma unroll
-  for (int q = 0; q < TileRegs<D>::VK; ++q) {
-    bool ok;
-    int tok = key_token<WIN>(tile * kAttnBN + kg * TileRegs<D>::VK + q, nkv, r, Gw, br, R, ok);
-    t.v[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)tok * D + dc * 8);
+    int key = min(tile * BN + row, nkv - 1);
+    t.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * D + col * 8);
+    t.v[i] = *reinterpret_cast<const u32x4*>(vtbase + (int64_t)tile * D * BN + c * 8);
   }
 }
 
 template <int D>
 __device__ __attribute__((always_inline)) inline void store_tile(const TileRegs<D>& t, u16* ks, u16* vt, int tid) {
-  constexpr int CPR = TileRegs<D>::CPR, VK = TileRegs<D>::VK;
-  constexpr int KS = D + 8, VS = kAttnBN + 8;
+  constexpr int CPR = D / 8;
+  constexpr int KS = D + 8, VS = BN + 8;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::K_CPT; ++i) {
+  for (int i = 0; i < TileRegs<D>::CH; ++i) {
     int c = tid + i * 256;
     int row = c / CPR, col = c - row * CPR;
     // key row r lives in LDS row perm(r) (bits 2 and 3 swapped): MFMA row m
@@ -178,31 +349,16 @@ __device__ __attribute__((always_inline)) inline void store_tile(const TileRegs<
     // read touch 8 consecutive rows, i.e. distinct banks
     int prow = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
     *reinterpret_cast<u32x4*>(ks + prow * KS + col * 8) = t.k[i];
-  }
-  constexpr int KG = kAttnBN / VK;
-  int kg = tid % KG, dc = tid / KG;
-#pragma unroll
-  for (int jd = 0; jd < 8; ++jd) {
-    unsigned e[VK];
-#pragma unroll
-    for (int q = 0; q < VK; ++q) {
-      const unsigned w = t.v[q][jd >> 1];
-      e[q] = (jd & 1) ? (w >> 16) : (w & 0xFFFFu);
-    }
-    u16* dst = vt + (dc * 8 + jd) * VS + kg * VK;
-    if constexpr (VK == 4) {
-      u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-      *reinterpret_cast<u32x2*>(dst) = pk;
-    } else {
-      *reinterpret_cast<unsigned*>(dst) = e[0] | (e[1] << 16);
-    }
+    int d = c / (BN / 8), k8 = c - d * (BN / 8);
+    *reinterpret_cast<u32x4*>(vt + d * VS + k8 * 8) = t.v[i];
   }
 }
 
 // S^T (keys x queries) of one tile for the wave's QG groups of 32 queries.
+// MFMA row n reads LDS row n, which holds key perm(n).
 template <int D, int QG>
-__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG][2], const u16* ks, int krow_perm,
-                                                                  int hi, const f16x8 (&qf)[QG][D / 16]) {
+__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG][2], const u16* ks, int n, int hi,
+                                                                  const f16x8 (&qf)[QG][D / 16]) {
   constexpr int KS = D + 8;
 #pragma unroll
   for (int g = 0; g < QG; ++g)
@@ -210,7 +366,7 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
-  const u16* kr = ks + krow_perm * KS + 8 * hi;  // krow_perm: LDS row of MFMA row n
+  const u16* kr = ks + n * KS + 8 * hi;
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
 #pragma unroll
@@ -226,7 +382,7 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void tile_pv(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
                                                               const f16x8 (&pf)[QG][4]) {
-  constexpr int VS = kAttnBN + 8;
+  constexpr int VS = BN + 8;
   const u16* vr = vt + n * VS + 8 * hi;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -239,25 +395,19 @@ __device__ __attribute__((always_inline)) inline void tile_pv(f32x16 (&o)[QG][D 
   }
 }
 
-// Keys of the tile that are not valid (tail of the key set, bridge tokens
-// already inside the Halo rectangle) get a -inf score.  vm holds one bit per
-// key of the tile; S^T register 8*jj + i of block kb is key
-// 32 kb + 16 jj + 8 hi + i.
+// Keys at or beyond `valid` (tail of the last tile) get a -inf score.  S^T
+// register 8*jj + i of block kb is key 32 kb + 16 jj + 8 hi + i.
 template <int QG>
-__device__ __attribute__((always_inline)) inline void mask_scores(f32x16 (&s)[QG][2], uint64_t vm, int hi) {
-  const uint32_t lm0 = (uint32_t)(vm >> (8 * hi));
-  const uint32_t lm1 = (uint32_t)(vm >> (32 + 8 * hi));
+__device__ __attribute__((always_inline)) inline void mask_tail(f32x16 (&s)[QG][2], int valid, int hi) {
 #pragma unroll
   for (int g = 0; g < QG; ++g)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint32_t bits = kb ? lm1 : lm0;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int bit = 16 * (i >> 3) + (i & 7);
-        s[g][kb][i] = ((bits >> bit) & 1u) ? s[g][kb][i] : -INFINITY;
+        int key = 32 * kb + 16 * (i >> 3) + 8 * hi + (i & 7);
+        s[g][kb][i] = key < valid ? s[g][kb][i] : -INFINITY;
       }
-    }
 }
 
 // Combine a value with the one held by the lane 32 apart (the other half of
@@ -335,32 +485,29 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
   const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
   int64_t bh;
   int qtile = 0, rec = 0;
-  WinRect r = {};
+  int qy0 = 0, qx0 = 0, qh = 0, qw = 1;
   int nq, nkv;
+  int64_t t0 = 0;  // first key tile of the item's key set
   if constexpr (WIN) {
     bh = L / a.max_items;
     int64_t it = L - bh * a.max_items;
-    if (bh >= a.BH || it >= *a.n_items) return;
+    if (bh >= a.BH || it >= a.n_items[0]) return;
     rec = a.items[2 * it];
     qtile = a.items[2 * it + 1];
     const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
-    r.qy0 = rp[0]; r.qx0 = rp[1]; r.qh = rp[2]; r.qw = rp[3];
-    r.ky0 = rp[4]; r.kx0 = rp[5]; r.kh = rp[6]; r.kw = rp[7];
-    r.kwd = FastDiv::make(r.kw);
-    r.gwd = FastDiv::make(a.Gw);
-    nq = r.qh * r.qw;
-    nkv = r.kh * r.kw + a.R;
+    qy0 = rp[0]; qx0 = rp[1]; qh = rp[2]; qw = rp[3];
+    nq = qh * qw;
+    nkv = rp[6] * rp[7] + (a.R > 0 ? a.bcount[(int64_t)rec * a.BH + bh] : 0);
+    t0 = a.kv_tile_off[rec];
   } else {
     bh = L / a.n_qtiles;
     qtile = (int)(L - bh * a.n_qtiles);
     if (bh >= a.BH) return;
     nq = a.Nq;
-    nkv = a.Nk;
+    nkv = a.n_kv;
   }
-  const int32_t* br = (WIN && a.R > 0) ? a.bridge + bh * a.R : nullptr;
-  const int64_t kv_rows = WIN ? (int64_t)a.Nq : (int64_t)a.Nk;
-  const u16* kbase = a.k + bh * kv_rows * D;
-  const u16* vbase = a.v + bh * kv_rows * D;
+  const u16* kbase = a.k + bh * a.k_rows * D + t0 * BN * D;
+  const u16* vtbase = a.vt + (bh * a.k_tiles + t0) * (int64_t)D * BN;
   const u16* qbase = a.q + bh * (int64_t)a.Nq * D;
 
   // ---- queries of this lane
@@ -371,9 +518,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
     int t = qtile * BM + wave * 32 * QG + 32 * g + n;
     qvalid[g] = t < nq;
     if constexpr (WIN) {
-      int yy = qvalid[g] ? t / r.qw : 0;
-      int xx = qvalid[g] ? t - yy * r.qw : 0;
-      qtok[g] = (r.qy0 + yy) * a.Gw + r.qx0 + xx;
+      int yy = qvalid[g] ? t / qw : 0;
+      int xx = qvalid[g] ? t - yy * qw : 0;
+      qtok[g] = (qy0 + yy) * a.Gw + qx0 + xx;
     } else {
       qtok[g] = qvalid[g] ? t : 0;
     }
@@ -388,10 +535,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
 
   const int nt = (nkv + BN - 1) / BN;
   const float c = a.c;
-  // MFMA row n of the score tile is key perm(n) (bits 2 and 3 swapped), so
-  // that S^T registers 8*jj + i of block kb hold key 32 kb + 16 jj + 8 hi + i;
-  // store_tile already placed key perm(n) in LDS row n.
-  const int krow_perm = n;
 
   f32x16 o[QG][DB];
   float m_run[QG], l_run[QG];
@@ -407,23 +550,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
 
   // ---- prologue: tile 0 to LDS, tile 1 in flight
   TileRegs<D> tr;
-  load_tile<D, WIN>(tr, 0, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
+  load_tile<D>(tr, 0, tid, nkv, kbase, vtbase);
   store_tile<D>(tr, smem, smem + K_ELEMS, tid);
-  load_tile<D, WIN>(tr, 1, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
+  load_tile<D>(tr, nt > 1 ? 1 : 0, tid, nkv, kbase, vtbase);
   __syncthreads();
 
   for (int j = 0; j < nt; ++j) {
     u16* ks = smem + (j & 1) * STAGE;
     u16* vt = ks + K_ELEMS;
-    uint64_t vm;
-    {
-      bool ok;
-      (void)key_token<WIN>(j * BN + lane, nkv, r, a.Gw, br, a.R, ok);
-      vm = __ballot(ok);
-    }
     f32x16 s[QG][2];
-    tile_scores<D, QG>(s, ks, krow_perm, hi, qf);
-    if (vm != ~0ull) mask_scores<QG>(s, vm, hi);
+    tile_scores<D, QG>(s, ks, n, hi, qf);
+    const int valid = nkv - j * BN;
+    if (valid < BN) mask_tail<QG>(s, valid, hi);
     float alpha[QG];
     f16x8 pf[QG][4];
     tile_softmax<QG>(s, c, m_run, l_run, alpha, pf);
@@ -442,7 +580,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
     if (j + 1 < nt) {
       u16* ks2 = smem + ((j + 1) & 1) * STAGE;
       store_tile<D>(tr, ks2, ks2 + K_ELEMS, tid);
-      load_tile<D, WIN>(tr, j + 2, tid, nkv, r, a.Gw, br, a.R, kbase, vbase);
+      load_tile<D>(tr, j + 2 < nt ? j + 2 : j + 1, tid, nkv, kbase, vtbase);
     }
     __syncthreads();
   }
@@ -453,36 +591,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
     float lt = pair_sum(l_run[g]);
     float inv = 1.0f / lt;
     if (!qvalid[g]) continue;
+    bool direct = true;
+    int t = 0;
     if constexpr (WIN) {
-      int t = qtile * BM + wave * 32 * QG + 32 * g + n;
-      int uy = t / r.qw, ux = t - (t / r.qw) * r.qw;
-      int wt = min(uy + 1, r.qh - uy) * min(ux + 1, r.qw - ux);
-      int tok = qtok[g];
-      if (a.wsum[tok] == wt) {
-        u16* orow = a.out + (bh * (int64_t)a.Nq + tok) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            int d = 32 * db + 8 * q4 + 4 * hi;
-            uint2 pk;
-            pk.x = (unsigned)f2bf(o[g][db][4 * q4 + 0] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 1] * inv) << 16);
-            pk.y = (unsigned)f2bf(o[g][db][4 * q4 + 2] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 3] * inv) << 16);
-            *reinterpret_cast<uint2*>(orow + d) = pk;
-          }
-      } else {
-        float* srow = a.slots + ((int64_t)(a.slot_off[rec] + t) * a.BH + bh) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            int d = 32 * db + 8 * q4 + 4 * hi;
-            float4 v4 = make_float4(o[g][db][4 * q4 + 0] * inv, o[g][db][4 * q4 + 1] * inv,
-                                    o[g][db][4 * q4 + 2] * inv, o[g][db][4 * q4 + 3] * inv);
-            *reinterpret_cast<float4*>(srow + d) = v4;
-          }
-      }
-    } else {
+      t = qtile * BM + wave * 32 * QG + 32 * g + n;
+      int uy = t / qw, ux = t - (t / qw) * qw;
+      int wt = min(uy + 1, qh - uy) * min(ux + 1, qw - ux);
+      direct = a.wsum[qtok[g]] == wt;
+    }
+    if (direct) {
       u16* orow = a.out + (bh * (int64_t)a.Nq + qtok[g]) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -494,75 +611,22 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
           pk.y = (unsigned)f2bf(o[g][db][4 * q4 + 2] * inv) | ((unsigned)f2bf(o[g][db][4 * q4 + 3] * inv) << 16);
           *reinterpret_cast<uint2*>(orow + d) = pk;
         }
+    } else {
+      float* srow = a.slots + ((int64_t)(a.slot_off[rec] + t) * a.BH + bh) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int d = 32 * db + 8 * q4 + 4 * hi;
+          float4 v4 = make_float4(o[g][db][4 * q4 + 0] * inv, o[g][db][4 * q4 + 1] * inv,
+                                  o[g][db][4 * q4 + 2] * inv, o[g][db][4 * q4 + 3] * inv);
+          *reinterpret_cast<float4*>(srow + d) = v4;
+        }
     }
   }
 }
 
-// ------------------------------------------------------------ work list --
-// Items workspace: [0] n_items, then slot_off[max_windows],
-// rec_start[n_base], items[max_items][2].
-struct ItemsWs {
-  int* n_items;
-  int* slot_off;
-  int* rec_start;
-  int* items;
-};
-
-ItemsWs make_items_ws(void* ws, int max_windows, int n_base) {
-  ItemsWs w;
-  char* p = (char*)ws;
-  w.n_items = (int*)p;
-  p += align_up(sizeof(int));
-  w.slot_off = (int*)p;
-  p += align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1));
-  w.rec_start = (int*)p;
-  p += align_up(sizeof(int) * (n_base > 0 ? n_base : 1));
-  w.items = (int*)p;
-  return w;
-}
-
-// One block: slot offsets (prefix of query areas in record order), the
-// first record of every base window, and the (record, query tile) list with
-// whole windows first and quadrants after (largest key sets first).
-__global__ __launch_bounds__(256) void items_kernel(const int32_t* __restrict__ plan, ItemsWs w, int BM,
-                                                    int max_windows, int64_t max_items) {
-  __shared__ int s_item_off[4 * kMaxAxisWindows * kMaxAxisWindows];
-  int nwin = plan[AREA_PH_NWIN];
-  if (nwin > max_windows) nwin = max_windows;
-  if (threadIdx.x == 0) {
-    int qs = 0, it = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int i = 0; i < nwin; ++i) {
-        const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
-        bool quad = rp[9] >= 0;
-        if ((pass == 0) == quad) continue;
-        s_item_off[i] = it;
-        it += (rp[2] * rp[3] + BM - 1) / BM;
-      }
-    }
-    for (int i = 0; i < nwin; ++i) {
-      const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
-      w.slot_off[i] = qs;
-      qs += rp[2] * rp[3];
-      if (rp[9] <= 0) w.rec_start[rp[8]] = i;
-    }
-    if (it > max_items) it = (int)max_items;
-    *w.n_items = it;
-  }
-  __syncthreads();
-  for (int i = 0; i < nwin; ++i) {
-    const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * i;
-    int nt = (rp[2] * rp[3] + BM - 1) / BM;
-    for (int t = threadIdx.x; t < nt; t += blockDim.x) {
-      int idx = s_item_off[i] + t;
-      if (idx < max_items) {
-        w.items[2 * idx] = i;
-        w.items[2 * idx + 1] = t;
-      }
-    }
-  }
-}
-
+// ------------------------------------------------------------------ blend --
 struct BlendArgs {
   int Gh, Gw, D, ny, nx, Ly, Lx;
   int64_t BH;
@@ -671,53 +735,95 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
 
 }  // namespace
 
-int launch_dense_attn(const void* q_rot, const void* k_rot, const void* v, void* out, int64_t BH, int Nq,
-                      int Nk, int D, stream_t s) {
+size_t vt_bytes(int64_t BH, int M, int D) { return (size_t)BH * ((M + BN - 1) / BN) * BN * D * 2; }
+
+int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, stream_t s) {
+  if (BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
+  int tiles = (M + BN - 1) / BN;
+  dim3 grid((unsigned)tiles, (unsigned)BH);
+  hipStream_t st = (hipStream_t)s;
+  if (D == 128) {
+    if (bf16_in) hipLaunchKernelGGL((vt_kernel<128, true>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+    else hipLaunchKernelGGL((vt_kernel<128, false>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+  } else {
+    if (bf16_in) hipLaunchKernelGGL((vt_kernel<64, true>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+    else hipLaunchKernelGGL((vt_kernel<64, false>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+  }
+  return check_launch("vt_kernel");
+}
+
+int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH, int Nq, int Nk,
+                      int D, stream_t s) {
   AttnArgs a = {};
   a.q = (const u16*)q_rot;
   a.k = (const u16*)k_rot;
-  a.v = (const u16*)v;
+  a.vt = (const u16*)vt;
   a.out = (u16*)out;
   a.BH = BH;
   a.Nq = Nq;
-  a.Nk = Nk;
+  a.k_rows = Nk;
+  a.k_tiles = (Nk + BN - 1) / BN;
+  a.n_kv = Nk;
   a.n_qtiles = (Nq + kAttnBM - 1) / kAttnBM;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
   return launch_attn<false>(a, D, (int64_t)a.n_qtiles * BH, (hipStream_t)s);
 }
 
-size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base) {
-  return align_up(sizeof(int)) + align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1)) +
-         align_up(sizeof(int) * (n_base > 0 ? n_base : 1)) + align_up(sizeof(int) * 2 * (max_items > 0 ? max_items : 1));
+size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base, int64_t max_gtiles) {
+  return align_up(2 * sizeof(int)) + 2 * align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1)) +
+         align_up(sizeof(int) * (n_base > 0 ? n_base : 1)) + align_up(sizeof(int) * 2 * (max_items > 0 ? max_items : 1)) +
+         align_up(sizeof(int) * 2 * (max_gtiles > 0 ? max_gtiles : 1));
 }
 
 int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32_t* wsum, const int32_t* bridge_idx,
-                       const void* q_rot, const void* k_rot, const void* v, void* out, void* items_ws, float* slots,
-                       stream_t s) {
+                       const void* q_rot, const void* k_rot, const void* v, void* out, const WindowWs& ws, stream_t s) {
   hipStream_t st = (hipStream_t)s;
   int n_base = w.ny * w.nx;
-  ItemsWs iw = make_items_ws(items_ws, w.max_windows, n_base);
-  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(256), 0, st, plan, iw, kAttnBM, w.max_windows, w.max_items);
+  const int R = bridge_idx ? w.R : 0;
+  if (w.BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
+  ItemsWs iw = make_items_ws(ws.items, w.max_windows, n_base, w.max_items);
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(256), 0, st, plan, iw, kAttnBM, R, w.max_windows, w.max_items,
+                     w.max_gtiles);
   int rc = check_launch("items_kernel");
+  if (rc) return rc;
+  if (R > 0) {
+    hipLaunchKernelGGL(bridge_compact_kernel, dim3((unsigned)w.max_windows, (unsigned)w.BH), dim3(256), 0, st, plan,
+                       bridge_idx, ws.blist, ws.bcount, R, w.Gw, w.BH);
+    rc = check_launch("bridge_compact_kernel");
+    if (rc) return rc;
+  }
+  const int N = w.Gh * w.Gw;
+  dim3 gg((unsigned)w.max_gtiles, (unsigned)w.BH);
+  if (w.D == 128)
+    hipLaunchKernelGGL((gather_kernel<128>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
+                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
+                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.Gw, N, w.BH);
+  else
+    hipLaunchKernelGGL((gather_kernel<64>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
+                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
+                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.Gw, N, w.BH);
+  rc = check_launch("gather_kernel");
   if (rc) return rc;
   AttnArgs a = {};
   a.q = (const u16*)q_rot;
-  a.k = (const u16*)k_rot;
-  a.v = (const u16*)v;
+  a.k = (const u16*)ws.kg;
+  a.vt = (const u16*)ws.vg;
   a.out = (u16*)out;
   a.BH = w.BH;
-  a.Nq = w.Gh * w.Gw;
-  a.Nk = w.Gh * w.Gw;
+  a.Nq = N;
+  a.k_rows = w.max_gtiles * BN;
+  a.k_tiles = w.max_gtiles;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)w.D));
   a.plan = plan;
   a.wsum = wsum;
-  a.bridge = bridge_idx;
   a.items = iw.items;
   a.n_items = iw.n_items;
   a.slot_off = iw.slot_off;
-  a.slots = slots;
+  a.kv_tile_off = iw.kv_tile_off;
+  a.bcount = ws.bcount;
+  a.slots = ws.slots;
   a.Gw = w.Gw;
-  a.R = bridge_idx ? w.R : 0;
+  a.R = R;
   a.max_items = w.max_items;
   rc = launch_attn<true>(a, w.D, w.max_items * w.BH, st);
   if (rc) return rc;
@@ -734,9 +840,8 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
     b.ys[i] = w.ys[i];
     b.xs[i] = w.xs[i];
   }
-  int64_t N = (int64_t)w.Gh * w.Gw;
   hipLaunchKernelGGL(blend_kernel, dim3((unsigned)((N + kBlendTok - 1) / kBlendTok)), dim3(256), 0, st, b, plan,
-                     (const int*)iw.rec_start, (const int*)iw.slot_off, wsum, (const float*)slots, (u16*)out);
+                     (const int*)iw.rec_start, (const int*)iw.slot_off, wsum, (const float*)ws.slots, (u16*)out);
   return check_launch("blend_kernel");
 }
 
