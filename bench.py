@@ -69,6 +69,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="flux-6144")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one elementwise kernel over 512 MiB before the warm-up (known "
+                         "traffic, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -178,6 +181,15 @@ def main():
             flops[s] = 4.0 * D * pairs
     full_flops = 4.0 * D * BH * float(N) * N
 
+    if args.copy_calibration:
+        # one elementwise kernel with a unique name: reads 512 MiB, writes 512 MiB
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] calibration kernel (bitwise_not): 512 MiB read, 512 MiB written")
+        del src, dst
+
     log(f"[bench] warmup x{args.warmup}")
     for _ in range(args.warmup):
         one_pass([])
@@ -284,13 +296,36 @@ def main():
             "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(win_tflops / PEAK_MFMA_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "launches_per_step": n_win,
             "avg_launch_ms": round(agg["window_kernel"] / max(n_win, 1), 4),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the windowed attention kernel from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was taken on
+    the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_window_{workload}_traffic.md")
+    src = os.path.join(ROOT, "resolution_diffusion_transformer_amd", "csrc", "k_attn.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k_, v_ = line.split(":", 1)
+            fields[k_.strip().lstrip("-* ").strip("`")] = v_.strip().strip("`")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("k_attn.hip sha256") != sha:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
