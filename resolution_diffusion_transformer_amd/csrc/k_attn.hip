@@ -17,9 +17,11 @@
 //    v_permlane32_swap with the partner lane.  K rows sit in LDS in the
 //    order that makes the S^T accumulator registers the fp16 B operand of
 //    O^T += V^T P^T, so P never leaves registers.
-//  * K and V^T tiles are staged through LDS (double-buffered, padded rows,
-//    conflict-free 128-bit accesses) with the next tile's global loads in
-//    flight; one barrier per tile.  Four waves of 32 queries use ~220 VGPRs,
+//  * K and V^T tiles reach LDS by global->LDS DMA (global_load_lds_dwordx4,
+//    no register staging), double-buffered: the next tile's DMA runs under
+//    the current tile's compute; one barrier per tile.  Rows are unpadded and
+//    the 16-byte chunks XOR-swizzled by row, so the 128-bit MFMA operand
+//    reads are bank-conflict free.  Four waves of 32 queries use ~230 VGPRs,
 //    so two work-groups share a CU and overlap each other's softmax (VALU)
 //    and MFMA phases.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
@@ -45,6 +47,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = kAttnBN;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
+// expcnt[6:4], lgkmcnt[11:8]): wait for every vector memory operation.
+constexpr int kVmcnt0 = 0x0F70;
 
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
@@ -313,65 +318,80 @@ struct AttnArgs {
   int64_t max_items;
 };
 
-// Per-thread staging of one 64-key tile: 16-byte chunks of K rows and of the
-// V^T tile.
-template <int D>
-struct TileRegs {
-  static constexpr int CH = BN * D / 8 / 256;  // chunks per thread (4 at D=128)
-  u32x4 k[CH];
-  u32x4 v[CH];
-};
-
-template <int D>
-__device__ __attribute__((always_inline)) inline void load_tile(TileRegs<D>& t, int tile, int tid, int nkv,
-                                                                const u16* kbase, const u16* vtbase) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::CH; ++i) {
-    int c = tid + i * 256;
-    int row = c / CPR, col = c - row * CPR;
-    int key = min(tile * BN + row, nkv - 1);
-    t.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * D + col * 8);
-    t.v[i] = *reinterpret_cast<const u32x4*>(vtbase + (int64_t)tile * D * BN + c * 8);
-  }
+// LDS tile layouts (one stage = one 64-key tile).  Rows are unpadded so that
+// a tile can be filled by global->LDS DMA (each lane of a wave writes 16
+// bytes at base + 16 * lane); bank conflicts are avoided by XOR-swizzling the
+// 16-byte chunk index with the row index instead:
+//  * K: row r (D*2 bytes) holds key perm(r) (bits 2 and 3 of r swapped, the
+//    MFMA row order of the score tile); logical chunk c sits at c ^ swz(r).
+//  * V^T: row d (64 keys, 128 bytes) of the transposed tile; logical chunk c
+//    (8 keys) sits at c ^ swz(d).
+// swz() makes the 8 (or 16) lanes served together by a 128-bit read hit
+// distinct banks under both the 32-bank and the 64-bank arrangement.
+template <int ROW_BYTES>
+__device__ __attribute__((always_inline)) inline int swz(int r) {
+  if constexpr (ROW_BYTES >= 256) return r & 15;
+  else return (r & 7) ^ ((r >> 3) & 1);
 }
 
+__device__ __attribute__((always_inline)) inline int key_perm(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Issue the DMA of tile `tile` into one LDS stage: K rows then V^T rows,
+// CH 16-byte chunks of each per thread.  Rows past the last key of the set
+// re-read the last key (their scores are masked).  `wave` is wave-uniform, so
+// the LDS addresses (M0) are scalar; global addresses are a scalar tile base
+// plus a 32-bit lane offset.
 template <int D>
-__device__ __attribute__((always_inline)) inline void store_tile(const TileRegs<D>& t, u16* ks, u16* vt, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int KS = D + 8, VS = BN + 8;
+__device__ __attribute__((always_inline)) inline void issue_tile(u16* ks, u16* vt, int tile, int tid, int wave,
+                                                                 int nkv, const u16* kbase, const u16* vtbase) {
+  constexpr int KCH = D / 8;          // 16-byte chunks per K row
+  constexpr int VCH = BN / 8;         // 16-byte chunks per V^T row
+  constexpr int CH = BN * D / 8 / 256;
+  const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)tile * BN * D);
+  const char* vtt = reinterpret_cast<const char*>(vtbase + (int64_t)tile * D * BN);
+  const int last = nkv - 1 - tile * BN;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::CH; ++i) {
-    int c = tid + i * 256;
-    int row = c / CPR, col = c - row * CPR;
-    // key row r lives in LDS row perm(r) (bits 2 and 3 swapped): MFMA row m
-    // then reads LDS row m, so the 8 lanes served together by a 128-bit
-    // read touch 8 consecutive rows, i.e. distinct banks
-    int prow = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
-    *reinterpret_cast<u32x4*>(ks + prow * KS + col * 8) = t.k[i];
-    int d = c / (BN / 8), k8 = c - d * (BN / 8);
-    *reinterpret_cast<u32x4*>(vt + d * VS + k8 * 8) = t.v[i];
+  for (int i = 0; i < CH; ++i) {
+    const int p = i * 256 + tid;      // LDS chunk written by this lane
+    const int r = p / KCH, pc = p - r * KCH;
+    const int c = pc ^ swz<D * 2>(r);
+    const unsigned off = (unsigned)(min(key_perm(r), last) * (D * 2) + c * 16);
+    __builtin_amdgcn_global_load_lds((gptr_t)(kt + off), (lptr_t)(ks + (i * 256 + wave * 64) * 8), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int p = i * 256 + tid;
+    const int d = p / VCH, pc = p - d * VCH;
+    const int c = pc ^ swz<BN * 2>(d);
+    const unsigned off = (unsigned)(d * (BN * 2) + c * 16);
+    __builtin_amdgcn_global_load_lds((gptr_t)(vtt + off), (lptr_t)(vt + (i * 256 + wave * 64) * 8), 16, 0, 0);
   }
 }
 
 // S^T (keys x queries) of one tile for the wave's QG groups of 32 queries.
-// MFMA row n reads LDS row n, which holds key perm(n).
+// MFMA row n of block kb reads LDS row 32 kb + n, which holds key
+// perm(32 kb + n).
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG][2], const u16* ks, int n, int hi,
                                                                   const f16x8 (&qf)[QG][D / 16]) {
-  constexpr int KS = D + 8;
 #pragma unroll
   for (int g = 0; g < QG; ++g)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[g][kb][i] = 0.0f;
-  const u16* kr = ks + n * KS + 8 * hi;
+  const int sw = swz<D * 2>(n);
 #pragma unroll
   for (int kd = 0; kd < D / 16; ++kd) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f16x8 af = *reinterpret_cast<const f16x8*>(kr + 32 * kb * KS + 16 * kd);
+      const u16* kr = ks + (32 * kb + n) * D + (((2 * kd + hi) ^ sw) * 8);
+      f16x8 af = *reinterpret_cast<const f16x8*>(kr);
 #pragma unroll
       for (int g = 0; g < QG; ++g) s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, qf[g][kd], s[g][kb], 0, 0, 0);
     }
@@ -382,13 +402,13 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void tile_pv(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
                                                               const f16x8 (&pf)[QG][4]) {
-  constexpr int VS = BN + 8;
-  const u16* vr = vt + n * VS + 8 * hi;
+  const int sw = swz<BN * 2>(n);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      f16x8 af = *reinterpret_cast<const f16x8*>(vr + 32 * db * VS + 16 * ks);
+      const u16* vr = vt + (32 * db + n) * BN + (((2 * ks + hi) ^ sw) * 8);
+      f16x8 af = *reinterpret_cast<const f16x8*>(vr);
 #pragma unroll
       for (int g = 0; g < QG; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[g][ks], o[g][db], 0, 0, 0);
     }
@@ -466,15 +486,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
   constexpr int BM = kAttnBM;     // 4 waves x QG groups x 32 queries
   constexpr int KD = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KS = D + 8;
-  constexpr int VS = BN + 8;
-  constexpr int K_ELEMS = BN * KS;
-  constexpr int V_ELEMS = D * VS;
-  constexpr int STAGE = K_ELEMS + V_ELEMS;
+  constexpr int K_ELEMS = BN * D;
+  constexpr int V_ELEMS = D * BN;
   static_assert(BM == 4 * 32 * QG, "query tile");
 
-  // two LDS stages: the tile being multiplied and the tile being written
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * STAGE];
+  // two LDS stages, as separate objects so that the compiler can tell a DMA
+  // into one stage from reads of the other
+  __shared__ __attribute__((aligned(16))) u16 ks0[K_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 vt0[V_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 ks1[K_ELEMS];
+  __shared__ __attribute__((aligned(16))) u16 vt1[V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -548,23 +569,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[g][db][i] = 0.0f;
   }
 
-  // ---- prologue: tile 0 to LDS, tile 1 in flight
-  TileRegs<D> tr;
-  load_tile<D>(tr, 0, tid, nkv, kbase, vtbase);
-  store_tile<D>(tr, smem, smem + K_ELEMS, tid);
-  load_tile<D>(tr, nt > 1 ? 1 : 0, tid, nkv, kbase, vtbase);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    u16* ks = smem + (j & 1) * STAGE;
-    u16* vt = ks + K_ELEMS;
-    f32x16 s[QG][2];
-    tile_scores<D, QG>(s, ks, n, hi, qf);
+  // One tile: scores, softmax, O update.
+  auto compute = [&](const u16* ks, const u16* vt, int j) __attribute__((always_inline)) {
+    f32x16 sc[QG][2];
+    tile_scores<D, QG>(sc, ks, n, hi, qf);
     const int valid = nkv - j * BN;
-    if (valid < BN) mask_tail<QG>(s, valid, hi);
+    if (valid < BN) mask_tail<QG>(sc, valid, hi);
     float alpha[QG];
     f16x8 pf[QG][4];
-    tile_softmax<QG>(s, c, m_run, l_run, alpha, pf);
+    tile_softmax<QG>(sc, c, m_run, l_run, alpha, pf);
     bool resc = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) resc |= alpha[g] != 1.0f;
@@ -577,11 +590,28 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
           for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha[g];
     }
     tile_pv<D, QG>(o, vt, n, hi, pf);
-    if (j + 1 < nt) {
-      u16* ks2 = smem + ((j + 1) & 1) * STAGE;
-      store_tile<D>(tr, ks2, ks2 + K_ELEMS, tid);
-      load_tile<D>(tr, j + 2 < nt ? j + 2 : j + 1, tid, nkv, kbase, vtbase);
-    }
+  };
+
+  // Tile j lives in stage j % 2.  Each half-iteration starts the DMA of the
+  // next tile into the other stage, computes tile j, then waits for its own
+  // DMAs and syncs: the next tile has landed for every wave and stage j % 2
+  // is free.  No DMA is outstanding at a branch merge, which keeps the
+  // compiler's LDS-DMA wait tracking exact (no wait before reading a stage).
+  // The last half-iteration re-loads the last tile into the idle stage
+  // instead of branching around the DMA.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  issue_tile<D>(ks0, vt0, 0, tid, wave_u, nkv, kbase, vtbase);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  for (int j = 0; j < nt; j += 2) {
+    issue_tile<D>(ks1, vt1, min(j + 1, nt - 1), tid, wave_u, nkv, kbase, vtbase);
+    compute(ks0, vt0, j);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    if (j + 1 >= nt) break;
+    issue_tile<D>(ks0, vt0, min(j + 2, nt - 1), tid, wave_u, nkv, kbase, vtbase);
+    compute(ks1, vt1, j + 1);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
   }
 
