@@ -11,7 +11,11 @@ The reported value is AReA attention milliseconds per denoising step (the
 schedule's time divided by its 28 steps), timed over K bench steps after W
 warm-up steps with inputs already resident in HBM.  Prints one JSON line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--ablation]
+
+--ablation prints, instead of the bench line, the schedule's time with the
+quadrant splits, the Halo or the bridge turned off, and at a fixed smallest
+window, each against the same full-attention baseline.
 """
 from __future__ import annotations
 
@@ -62,6 +66,145 @@ class HipEvents:
         return float(ms.value)
 
 
+class Schedule:
+    """One problem's buffers, algorithmic work and timed pass over the whole
+    schedule (coarse steps, window steps and optionally one full call)."""
+
+    def __init__(self, A, wl, p, q, k, v, lat, out, ev):
+        import torch
+        self.A, self.wl, self.p, self.q, self.k, self.v, self.lat, self.out, self.ev = A, wl, p, q, k, v, lat, out, ev
+        A.area_validate(p)
+        dev = q.device
+        B, H, N, D = p.B, p.H, p.N, p.D
+        ws_bytes = max(A.area_workspace_bytes(p, op) for op in (A.OP_FULL, A.OP_COARSE, A.OP_PLAN, A.OP_WINDOW))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.plan = torch.zeros(A.area_plan_words(p), dtype=torch.int32, device=dev)
+        self.wsum = torch.empty(N, dtype=torch.int32, device=dev)
+        self.bridge = (torch.empty((B, H, p.bridge_k), dtype=torch.int32, device=dev) if p.bridge_k > 0 else None)
+        self.energy = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.float32, device=dev)
+        self.energy_q = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.int32, device=dev)
+        self.n_steps = p.p1_steps + p.p2_steps
+        self.sched = [A.area_step_info(p, s) for s in range(self.n_steps)]
+        fs = sorted({st["f"] for st in self.sched if st["phase"] == A.PHASE_COARSE})
+        self.kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev),
+                        torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev)) for f in fs}
+
+    @staticmethod
+    def _tev():
+        import torch
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def window_plan(self, s):
+        A, p = self.A, self.p
+        A.area_dwt_detail(p, self.lat, self.energy, self.energy_q)
+        A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, self.bridge, self.ws)
+
+    def one_pass(self, rec, full=True):
+        """Enqueue the whole hot path once; rec collects (kind, step, events)."""
+        A, p, ev, tev = self.A, self.p, self.ev, self._tev
+        for s, st in enumerate(self.sched):
+            if st["phase"] == A.PHASE_COARSE:
+                f = st["f"]
+                kp, vp = self.kpv[f]
+                e0 = tev()
+                A.area_pool_kv(p, f, self.k, self.v, kp, vp)
+                e1 = tev()
+                a0, a1 = ev.new(), ev.new()
+                A.area_set_attn_events(a0, a1)
+                A.area_coarse_attn(p, f, self.q, kp, vp, self.out, self.ws)
+                A.area_set_attn_events(None, None)
+                e2 = tev()
+                rec.append(("coarse", s, (e0, e1, e2, a0, a1)))
+            else:
+                e0 = tev()
+                A.area_dwt_detail(p, self.lat, self.energy, self.energy_q)
+                e1 = tev()
+                A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, self.bridge, self.ws)
+                e2 = tev()
+                a0, a1 = ev.new(), ev.new()
+                A.area_set_attn_events(a0, a1)
+                A.area_window_attn(p, s, self.plan, self.wsum, self.bridge, self.q, self.k, self.v, self.out, self.ws)
+                A.area_set_attn_events(None, None)
+                e3 = tev()
+                rec.append(("window", s, (e0, e1, e2, e3, a0, a1)))
+        if full:
+            e0 = tev()
+            a0, a1 = ev.new(), ev.new()
+            A.area_set_attn_events(a0, a1)
+            A.area_full_attn(p, self.q, self.k, self.v, self.out, self.ws)
+            A.area_set_attn_events(None, None)
+            e1 = tev()
+            rec.append(("full", -1, (e0, e1, a0, a1)))
+
+    def count(self):
+        """Algorithmic FLOPs per step (deterministic: plans depend only on the
+        inputs) and the (query, key) pairs of every window step."""
+        A, p = self.A, self.p
+        D, BH, N, Gw = p.D, p.B * p.H, p.N, p.Gw
+        flops, win_pairs = {}, {}
+        for s, st in enumerate(self.sched):
+            if st["phase"] == A.PHASE_COARSE:
+                flops[s] = 4.0 * D * BH * N * (N // (st["f"] ** 2))
+                continue
+            self.window_plan(s)
+            pl = self.plan.cpu().numpy()
+            nwin = int(pl[0])
+            recs = pl[A.PLAN_HEADER:A.PLAN_HEADER + A.PLAN_REC * nwin].reshape(nwin, A.PLAN_REC)
+            if self.bridge is not None:
+                br = self.bridge.cpu().numpy().reshape(BH, -1)
+                by, bx = br // Gw, br % Gw
+            pairs = 0
+            for r in recs:
+                qy0, qx0, qh, qw, ky0, kx0, kh, kw = (int(x) for x in r[:8])
+                nkv = kh * kw * BH
+                if self.bridge is not None:
+                    inside = (by >= ky0) & (by < ky0 + kh) & (bx >= kx0) & (bx < kx0 + kw)
+                    nkv += int((~inside).sum())
+                pairs += qh * qw * nkv
+            win_pairs[s] = pairs
+            flops[s] = 4.0 * D * pairs
+        self.flops, self.win_pairs = flops, win_pairs
+        self.full_flops = 4.0 * D * BH * float(N) * N
+        return flops
+
+    def summarize(self, recs, K):
+        """Per-phase times averaged over K passes."""
+        A, ev = self.A, self.ev
+        agg = {k_: 0.0 for k_ in ("pool", "coarse_call", "coarse_kernel", "dwt", "plan", "window_call",
+                                   "window_kernel", "full_call", "full_kernel")}
+        per_step = {}
+        for kind, s, e in recs:
+            if kind == "coarse":
+                e0, e1, e2, a0, a1 = e
+                t_pool, t_call, t_ker = e0.elapsed_time(e1), e1.elapsed_time(e2), ev.elapsed(a0, a1)
+                agg["pool"] += t_pool
+                agg["coarse_call"] += t_call
+                agg["coarse_kernel"] += t_ker
+                per_step.setdefault(s, []).append(t_pool + t_call)
+            elif kind == "window":
+                e0, e1, e2, e3, a0, a1 = e
+                t_dwt, t_plan, t_call = e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3)
+                agg["dwt"] += t_dwt
+                agg["plan"] += t_plan
+                agg["window_call"] += t_call
+                agg["window_kernel"] += ev.elapsed(a0, a1)
+                per_step.setdefault(s, []).append(t_dwt + t_plan + t_call)
+            else:
+                e0, e1, a0, a1 = e
+                agg["full_call"] += e0.elapsed_time(e1)
+                agg["full_kernel"] += ev.elapsed(a0, a1)
+        for k_ in agg:
+            agg[k_] /= K
+        area_ms = agg["pool"] + agg["coarse_call"] + agg["dwt"] + agg["plan"] + agg["window_call"]
+        return agg, per_step, area_ms
+
+
+def tflops(fl, ms):
+    return fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,12 +215,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one elementwise kernel over 512 MiB before the warm-up (known "
                          "traffic, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the bench line, print one JSON line with the AReA schedule timed "
+                         "as configured and with splits, halo or bridge turned off, and at fixed w=64")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import resolution_diffusion_transformer_amd as A
@@ -92,7 +237,6 @@ def main():
     dev = torch.device("cuda:0")
     wl = W.get(args.workload)
     p = A.problem_for(wl)
-    A.area_validate(p)
     B, H, N, D = wl.B, wl.H, wl.N, wl.D
     BH = B * H
 
@@ -100,86 +244,17 @@ def main():
     q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
     lat = torch.from_numpy(W.make_latent(wl)).to(dev)
     out = torch.empty_like(q)
-    ws_bytes = max(A.area_workspace_bytes(p, op) for op in (A.OP_FULL, A.OP_COARSE, A.OP_PLAN, A.OP_WINDOW))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    plan = torch.zeros(A.area_plan_words(p), dtype=torch.int32, device=dev)
-    wsum = torch.empty(N, dtype=torch.int32, device=dev)
-    bridge = torch.empty((B, H, wl.bridge_k), dtype=torch.int32, device=dev)
-    energy = torch.empty((wl.Gh // 2, wl.Gw // 2), dtype=torch.float32, device=dev)
-    energy_q = torch.empty((wl.Gh // 2, wl.Gw // 2), dtype=torch.int32, device=dev)
-    n_steps = wl.p1_steps + wl.p2_steps
-    sched = [A.area_step_info(p, s) for s in range(n_steps)]
-    fs = sorted({st["f"] for st in sched if st["phase"] == A.PHASE_COARSE})
-    kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev),
-               torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev)) for f in fs}
+    ev = HipEvents()
+    sc = Schedule(A, wl, p, q, k, v, lat, out, ev)
     torch.cuda.synchronize()
 
-    ev = HipEvents()
+    if args.ablation:
+        run_ablation(A, wl, sc, args)
+        return
 
-    def tev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def one_pass(rec):
-        """Enqueue the whole hot path once; rec collects (kind, step, events)."""
-        for s, st in enumerate(sched):
-            if st["phase"] == A.PHASE_COARSE:
-                f = st["f"]
-                kp, vp = kpv[f]
-                e0 = tev()
-                A.area_pool_kv(p, f, k, v, kp, vp)
-                e1 = tev()
-                a0, a1 = ev.new(), ev.new()
-                A.area_set_attn_events(a0, a1)
-                A.area_coarse_attn(p, f, q, kp, vp, out, ws)
-                A.area_set_attn_events(None, None)
-                e2 = tev()
-                rec.append(("coarse", s, (e0, e1, e2, a0, a1)))
-            else:
-                e0 = tev()
-                A.area_dwt_detail(p, lat, energy, energy_q)
-                e1 = tev()
-                A.area_window_plan(p, s, energy_q, k, plan, wsum, bridge, ws)
-                e2 = tev()
-                a0, a1 = ev.new(), ev.new()
-                A.area_set_attn_events(a0, a1)
-                A.area_window_attn(p, s, plan, wsum, bridge, q, k, v, out, ws)
-                A.area_set_attn_events(None, None)
-                e3 = tev()
-                rec.append(("window", s, (e0, e1, e2, e3, a0, a1)))
-        e0 = tev()
-        a0, a1 = ev.new(), ev.new()
-        A.area_set_attn_events(a0, a1)
-        A.area_full_attn(p, q, k, v, out, ws)
-        A.area_set_attn_events(None, None)
-        e1 = tev()
-        rec.append(("full", -1, (e0, e1, a0, a1)))
-
-    # ---- algorithmic work per step (deterministic: plans depend only on the inputs)
     log("[bench] counting algorithmic work")
-    flops = {}
-    win_pairs = {}
-    for s, st in enumerate(sched):
-        if st["phase"] == A.PHASE_COARSE:
-            flops[s] = 4.0 * D * BH * N * (N // (st["f"] ** 2))
-        else:
-            A.area_dwt_detail(p, lat, energy, energy_q)
-            A.area_window_plan(p, s, energy_q, k, plan, wsum, bridge, ws)
-            pl = plan.cpu().numpy()
-            br = bridge.cpu().numpy().reshape(BH, -1)
-            nwin = int(pl[0])
-            recs = pl[A.PLAN_HEADER:A.PLAN_HEADER + A.PLAN_REC * nwin].reshape(nwin, A.PLAN_REC)
-            by, bx = br // wl.Gw, br % wl.Gw
-            pairs = 0
-            for r in recs:
-                qy0, qx0, qh, qw, ky0, kx0, kh, kw = (int(x) for x in r[:8])
-                inside = (by >= ky0) & (by < ky0 + kh) & (bx >= kx0) & (bx < kx0 + kw)
-                nkv = kh * kw * BH + int((~inside).sum())
-                pairs += qh * qw * nkv
-            win_pairs[s] = pairs
-            flops[s] = 4.0 * D * pairs
-    full_flops = 4.0 * D * BH * float(N) * N
+    flops = sc.count()
+    sched, n_steps = sc.sched, sc.n_steps
 
     if args.copy_calibration:
         # one elementwise kernel with a unique name: reads 512 MiB, writes 512 MiB
@@ -192,7 +267,7 @@ def main():
 
     log(f"[bench] warmup x{args.warmup}")
     for _ in range(args.warmup):
-        one_pass([])
+        sc.one_pass([])
     torch.cuda.synchronize()
 
     log(f"[bench] timing x{args.steps}")
@@ -200,50 +275,23 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_pass(recs)
+        sc.one_pass(recs)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
 
-    # ---- per-phase times
-    agg = {k_: 0.0 for k_ in ("pool", "coarse_call", "coarse_kernel", "dwt", "plan", "window_call",
-                               "window_kernel", "full_call", "full_kernel")}
-    per_step = {}
-    for kind, s, e in recs:
-        if kind == "coarse":
-            e0, e1, e2, a0, a1 = e
-            t_pool, t_call, t_ker = e0.elapsed_time(e1), e1.elapsed_time(e2), ev.elapsed(a0, a1)
-            agg["pool"] += t_pool
-            agg["coarse_call"] += t_call
-            agg["coarse_kernel"] += t_ker
-            per_step.setdefault(s, []).append(t_pool + t_call)
-        elif kind == "window":
-            e0, e1, e2, e3, a0, a1 = e
-            t_dwt, t_plan, t_call, t_ker = e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3), ev.elapsed(a0, a1)
-            agg["dwt"] += t_dwt
-            agg["plan"] += t_plan
-            agg["window_call"] += t_call
-            agg["window_kernel"] += t_ker
-            per_step.setdefault(s, []).append(t_dwt + t_plan + t_call)
-        else:
-            e0, e1, a0, a1 = e
-            agg["full_call"] += e0.elapsed_time(e1)
-            agg["full_kernel"] += ev.elapsed(a0, a1)
     K = args.steps
-    for k_ in agg:
-        agg[k_] /= K
-    area_ms = agg["pool"] + agg["coarse_call"] + agg["dwt"] + agg["plan"] + agg["window_call"]
+    agg, per_step, area_ms = sc.summarize(recs, K)
     area_ms_per_step = area_ms / n_steps
     n_coarse = sum(1 for st in sched if st["phase"] == A.PHASE_COARSE)
     n_win = n_steps - n_coarse
     coarse_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_COARSE)
     win_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_WINDOW)
-    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
-    win_tflops = tf(win_fl, agg["window_kernel"])
-    coarse_tflops = tf(coarse_fl, agg["coarse_kernel"])
+    win_tflops = tflops(win_fl, agg["window_kernel"])
+    coarse_tflops = tflops(coarse_fl, agg["coarse_kernel"])
     full_ms = agg["full_call"]
-    full_tflops = tf(full_flops, agg["full_kernel"])
-    area_tflops = tf(coarse_fl + win_fl, area_ms)
+    full_tflops = tflops(sc.full_flops, agg["full_kernel"])
+    area_tflops = tflops(coarse_fl + win_fl, area_ms)
     # pooling bytes (mean mode): read K and V, write pooled K and V
     pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 2
                      for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
@@ -252,7 +300,7 @@ def main():
     # ---- CPU oracle baseline on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps)
+        cpu = cpu_baseline(wl, p, q, k, v, lat, sched, flops, sc.win_pairs, n_steps)
 
     phases = {
         "pool_ms_per_call": agg["pool"] / max(n_coarse, 1),
@@ -303,6 +351,43 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def run_ablation(A, wl, base, args):
+    """Attention-time ablations of the AReA schedule (quadrant splits off,
+    Halo off, bridge off, fixed smallest window), each against the same
+    full-attention baseline; prints one JSON line."""
+    import torch
+    variants = [("as configured", {}), ("no quadrant splits", {"split_num": 0}), ("no halo", {"halo": 0}),
+                ("no bridge", {"bridge_k": 0}), (f"fixed w={wl.w_min}", {"w_start": wl.w_min})]
+    rows = []
+    full_ms = None
+    for name, over in variants:
+        sc = base if not over else Schedule(A, wl, A.problem_for(wl, **over), base.q, base.k, base.v, base.lat,
+                                            base.out, base.ev)
+        log(f"[ablation] {name}")
+        flops = sc.count()
+        for _ in range(args.warmup):
+            sc.one_pass([], full=full_ms is None)
+        torch.cuda.synchronize()
+        recs = []
+        for _ in range(args.steps):
+            sc.one_pass(recs, full=full_ms is None)
+        torch.cuda.synchronize()
+        agg, _, area_ms = sc.summarize(recs, args.steps)
+        if full_ms is None:
+            full_ms = agg["full_call"]
+        win_fl = sum(flops[s_] for s_ in flops if sc.sched[s_]["phase"] == A.PHASE_WINDOW)
+        rows.append({"variant": name, "overrides": over,
+                     "ms_per_step": round(area_ms / sc.n_steps, 4),
+                     "speedup_vs_full": round(full_ms * sc.n_steps / area_ms, 3),
+                     "schedule_tflop": round(sum(flops.values()) / 1e12, 2),
+                     "window_kernel_tflops": round(tflops(win_fl, agg["window_kernel"]), 1)})
+        if sc is not base:
+            del sc
+            torch.cuda.empty_cache()
+    print(json.dumps({"ablation": rows, "workload": wl.name, "full_attn_ms": round(full_ms, 3),
+                      "steps": args.steps, "warmup": args.warmup, "unit": "ms/step"}), flush=True)
 
 
 def measured_traffic(workload):

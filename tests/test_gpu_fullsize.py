@@ -204,3 +204,64 @@ def test_repeated_calls_are_deterministic():
     for o in outs[1:]:
         for a, b in zip(o, outs[0]):
             assert torch.equal(a, b)
+
+
+# ------------------------------------------------ ablation knob settings --
+# The attention-time ablations of bench.py --ablation (quadrant splits off,
+# Halo off, bridge off, fixed smallest window) run the same kernels on plans
+# the oracle builds from the same knobs.
+
+ABLATIONS = {"no_splits": dict(split_num=0), "no_halo": dict(halo=0), "no_bridge": dict(bridge_k=0),
+             "fixed_w": dict(w_start=None)}
+
+
+@pytest.fixture(scope="module")
+def mid():
+    wl = W.get("flux-4096")
+    say(f"generating {wl.name} on the GPU (ablations)")
+    q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
+    lat = W.make_latent(wl)
+    yield wl, q, k, v, lat
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", sorted(ABLATIONS))
+def test_ablation_knobs(mid, name):
+    wl, q, k, v, lat = mid
+    over = dict(ABLATIONS[name])
+    if "w_start" in over:
+        over["w_start"] = wl.w_min
+    p = A.problem_for(wl, **over)
+    halo = over.get("halo", wl.halo)
+    R = over.get("bridge_k", wl.bridge_k)
+    split_num = over.get("split_num", 1)
+    w_start = over.get("w_start", wl.w_start)
+    _, Eq = A.area_dwt_detail(p, torch.from_numpy(lat).cuda())
+    Eq_ref = O.energy_fixed(O.detail_energy(lat))
+    heads = (2, wl.H - 1)
+    br_ref = {h: O.bridge_select(head(k, h)[0, 0], R, wl.Gh, wl.Gw) for h in heads} if R > 0 else None
+    sizes = O.window_sizes(w_start, wl.w_min, wl.p2_steps)
+    for t in (0, wl.p2_steps - 1):
+        s = wl.p1_steps + t
+        plan, wsum, br = A.area_window_plan(p, s, Eq, k)
+        out = A.area_window_attn(p, s, plan, wsum, br, q, k, v)
+        torch.cuda.synchronize()
+        ref = O.window_plan(wl.Gh, wl.Gw, sizes[t], halo, wl.seed, t, Eq_ref, split_num=split_num)
+        pl = plan.cpu().numpy()
+        nwin = int(pl[0])
+        assert nwin == len(ref.windows), (name, t)
+        np.testing.assert_array_equal(pl[16:16 + 10 * nwin].reshape(nwin, 10), ref.records())
+        np.testing.assert_array_equal(wsum.cpu().numpy(), ref.wsum)
+        if R == 0:
+            assert br is None
+        else:
+            b = br.cpu().numpy()
+            for h in heads:
+                np.testing.assert_array_equal(b[0, h], br_ref[h], err_msg=f"{name} bridge head {h}")
+        rows = rows_for(wl, ref, n_random=32, seed=40 + t)
+        for h in heads:
+            o_ref = O.window_attention(head(q, h), head(k, h), head(v, h), ref,
+                                       br_ref[h][None, None] if R > 0 else None,
+                                       wl.Gh, wl.Gw, wl.rope_theta, rows=rows)
+            close(head(out, h)[:, :, rows], o_ref, f"{wl.name} ablation {name} step {t} (w={sizes[t]}) head {h}")
