@@ -73,6 +73,7 @@ extern "C" {
 #define AREA_OP_COARSE 1
 #define AREA_OP_PLAN   2
 #define AREA_OP_WINDOW 3
+#define AREA_OP_STEP   4       /* area_attn_step: every intermediate of one step */
 
 /* Plan buffer layout (int32): AREA_PLAN_HEADER header words, then up to
  * max_windows records of AREA_PLAN_REC words each. */
@@ -243,6 +244,28 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
  * area_workspace_bytes(p, AREA_OP_FULL). */
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v,
                    void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One attention call of denoising step `step` along the schedule: the
+ * pages run Phase I (pooled coarse attention over the pooling ramp) for the
+ * first p1_steps denoising steps and Phase II (windowed attention) after
+ * that, and keep the original attention when the canvas is at or below the
+ * native size (ai.info summary, Methodology, Phase I and Phase II; README,
+ * setup note on native resolution).  Dispatches by area_step_info():
+ *  AREA_PHASE_FULL:   area_full_attn;
+ *  AREA_PHASE_COARSE: area_pool_kv with the step's factor f, then
+ *                     area_coarse_attn;
+ *  AREA_PHASE_WINDOW: area_dwt_detail of `latent` (C channels, [C][Gh][Gw]
+ *                     fp32; NULL: no quadrant splits), area_window_plan
+ *                     (with the bridge when p->bridge_k > 0) and
+ *                     area_window_attn.
+ * q, k, v: [B][H][Gh*Gw][D] bf16 un-rotated; out: same layout.  Every
+ * intermediate (pooled K/V, energy map, plan, weight sums, bridge indices)
+ * lives in the caller's workspace of area_workspace_bytes(p, AREA_OP_STEP)
+ * bytes; nothing is allocated.  Results are identical to calling the
+ * individual entry points in that order.  Errors as for those calls; on an
+ * error nothing further is enqueued. */
+int area_attn_step(const area_problem* p, int step, int C, const float* latent, const void* q,
+                   const void* k, const void* v, void* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

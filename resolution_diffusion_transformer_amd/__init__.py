@@ -18,14 +18,14 @@ __all__ = [
     "AreaError", "Problem", "lib", "library_path", "exported_symbols",
     "area_validate", "area_step_info", "area_f0", "area_base_windows", "area_workspace_bytes",
     "area_plan_words", "area_pool_kv", "area_coarse_attn", "area_dwt_detail",
-    "area_window_plan", "area_window_attn", "area_full_attn", "area_set_attn_events",
+    "area_window_plan", "area_window_attn", "area_full_attn", "area_attn_step", "area_set_attn_events",
     "POOL_MEAN", "POOL_CENTER", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
-    "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "PLAN_HEADER", "PLAN_REC",
+    "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "OP_STEP", "PLAN_HEADER", "PLAN_REC",
 ]
 
 POOL_MEAN, POOL_CENTER = 0, 1
 PHASE_FULL, PHASE_COARSE, PHASE_WINDOW = 0, 1, 2
-OP_FULL, OP_COARSE, OP_PLAN, OP_WINDOW = 0, 1, 2, 3
+OP_FULL, OP_COARSE, OP_PLAN, OP_WINDOW, OP_STEP = 0, 1, 2, 3, 4
 PLAN_HEADER, PLAN_REC = 16, 10
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -117,6 +117,8 @@ _SIGS = {
     "area_window_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 8
                          + [ctypes.c_size_t, ctypes.c_void_p]),
     "area_full_attn": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5
+                       + [ctypes.c_size_t, ctypes.c_void_p]),
+    "area_attn_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
                        + [ctypes.c_size_t, ctypes.c_void_p]),
 }
 
@@ -322,6 +324,27 @@ def area_window_attn(p: Problem, step: int, plan, wsum, bridge_idx, q, k, v, out
     _check(lib().area_window_attn(ref, step, _ptr(plan), _ptr(wsum), _ptr(bridge_idx), _ptr(q),
                                   _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream()))
+    return out
+
+
+def area_attn_step(p: Problem, step: int, latent, q, k, v, out=None, ws=None):
+    """One denoising step's attention along the schedule (full, pooled
+    coarse, or windowed with plan and bridge); latent [C, Gh, Gw] fp32 feeds
+    the detail map of window steps (None: no quadrant splits)."""
+    torch = _torch()
+    shp = (p.B, p.H, p.N, p.D)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, shp, nm)
+    C = 0
+    if latent is not None:
+        C = latent.shape[0]
+        _need(latent, torch.float32, (C, p.Gh, p.Gw), "latent")
+    out = torch.empty_like(q) if out is None else out
+    _need(out, torch.bfloat16, shp, "out")
+    ws = workspace(p, OP_STEP, q.device) if ws is None else ws
+    s, ref = _pp(p)
+    _check(lib().area_attn_step(ref, step, C, _ptr(latent), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream()))
     return out
 
 

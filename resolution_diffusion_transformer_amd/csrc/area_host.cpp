@@ -3,6 +3,7 @@
 // sizing and the C entry points that enqueue the kernels.
 #include <cmath>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -282,8 +283,62 @@ static WindowLayout window_layout(const area_problem& p) {
   return l;
 }
 
+// Intermediates of area_attn_step, carved from its workspace: coarse steps
+// hold the pooled K and V (largest for the smallest factor of the ramp);
+// window steps hold the energy map, plan, weight sums and bridge indices.
+// Each phase's own workspace follows its intermediates.
+struct StepLayout {
+  size_t kp = 0, vp = 0, coarse_ws = 0;                          // coarse
+  size_t energy = 0, energy_q = 0, plan = 0, wsum = 0, bridge = 0, window_ws = 0;  // window
+  size_t total = 0;
+};
+
+static size_t workspace_bytes(const area_problem& p, int op);
+
+static StepLayout step_layout(const area_problem& p) {
+  StepLayout l;
+  const size_t N = (size_t)N_of(p), BH = (size_t)BH_of(p);
+  if (canvas_gated(p)) {
+    l.total = workspace_bytes(p, AREA_OP_FULL);
+    return l;
+  }
+  size_t coarse = 0, window = 0;
+  if (p.p1_steps > 0) {
+    int f0 = p.f0 > 0 ? p.f0 : derive_f0(p);
+    size_t M = 0;
+    for (int s = 0; s < p.p1_steps; ++s) {
+      int f = ramp_factor(p, f0, s);
+      M = std::max(M, N / ((size_t)f * f));
+    }
+    const size_t pooled = align_up(BH * M * p.D * 2);
+    l.kp = 0;
+    l.vp = pooled;
+    l.coarse_ws = 2 * pooled;
+    coarse = l.coarse_ws + workspace_bytes(p, AREA_OP_COARSE);
+  }
+  if (p.p2_steps > 0) {
+    size_t o = 0;
+    l.energy = o;
+    o += align_up(N / 4 * 4);
+    l.energy_q = o;
+    o += align_up(N / 4 * 4);
+    l.plan = o;
+    o += align_up((AREA_PLAN_HEADER + (size_t)AREA_PLAN_REC * window_max(p).max_windows) * 4);
+    l.wsum = o;
+    o += align_up(N * 4);
+    l.bridge = o;
+    o += align_up(BH * std::max(p.bridge_k, 1) * 4);
+    l.window_ws = o;
+    window = o + std::max(workspace_bytes(p, AREA_OP_PLAN), workspace_bytes(p, AREA_OP_WINDOW));
+  }
+  l.total = std::max(coarse, window);
+  return l;
+}
+
 static size_t workspace_bytes(const area_problem& p, int op) {
   switch (op) {
+    case AREA_OP_STEP:
+      return step_layout(p).total;
     case AREA_OP_FULL:
       return 2 * align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)N_of(p), p.D));
     case AREA_OP_COARSE:
@@ -555,6 +610,46 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
                    stream);
   if (rc) return rc;
   return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, base + l.q, base + l.k, v, out, w, stream);
+}
+
+int area_attn_step(const area_problem* p, int step, int C, const float* latent, const void* q,
+                   const void* k, const void* v, void* out, void* ws, size_t ws_bytes, void* stream) {
+  area_step st;
+  int rc = area_step_info(p, step, &st);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
+  if (latent && C < 1) return fail(AREA_E_INVALID, "C must be >= 1");
+  rc = check_ws(*p, AREA_OP_STEP, ws, ws_bytes);
+  if (rc) return rc;
+  const StepLayout l = step_layout(*p);
+  char* base = (char*)ws;
+  switch (st.phase) {
+    case AREA_PHASE_FULL:
+      return area_full_attn(p, q, k, v, out, ws, ws_bytes, stream);
+    case AREA_PHASE_COARSE: {
+      void* kp = base + l.kp;
+      void* vp = base + l.vp;
+      rc = area_pool_kv(p, st.f, k, v, kp, vp, stream);
+      if (rc) return rc;
+      return area_coarse_attn(p, st.f, q, kp, vp, out, base + l.coarse_ws, ws_bytes - l.coarse_ws, stream);
+    }
+    default: {
+      float* energy = (float*)(base + l.energy);
+      int32_t* energy_q = (int32_t*)(base + l.energy_q);
+      int32_t* plan = (int32_t*)(base + l.plan);
+      int32_t* wsum = (int32_t*)(base + l.wsum);
+      int32_t* bridge = p->bridge_k > 0 ? (int32_t*)(base + l.bridge) : nullptr;
+      if (latent) {
+        rc = area_dwt_detail(p, C, latent, energy, energy_q, stream);
+        if (rc) return rc;
+      }
+      rc = area_window_plan(p, step, latent ? energy_q : nullptr, k, plan, wsum, bridge, base + l.window_ws,
+                            ws_bytes - l.window_ws, stream);
+      if (rc) return rc;
+      return area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
+                              ws_bytes - l.window_ws, stream);
+    }
+  }
 }
 
 }  // extern "C"

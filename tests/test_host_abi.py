@@ -184,3 +184,35 @@ def test_workspace_sizes():
                for t, w in enumerate(O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)))
     assert A.area_workspace_bytes(p, A.OP_WINDOW) >= 2 * tok + qmax * p.B * p.H * p.D * 4
     assert A.area_plan_words(p) == A.PLAN_HEADER + A.PLAN_REC * 4 * 36
+
+
+def test_step_workspace_covers_every_phase():
+    for name in ("tiny-32", "flux-2048", "flux-6144", "qwen-6144x2048"):
+        p = prob(name)
+        wl = W.get(name)
+        step = A.area_workspace_bytes(p, A.OP_STEP)
+        # window steps: energy map, plan, weight sums, bridge indices, then the larger
+        # of the plan and attention workspaces
+        win_min = max(A.area_workspace_bytes(p, A.OP_PLAN), A.area_workspace_bytes(p, A.OP_WINDOW))
+        win_min += 4 * A.area_plan_words(p) + 4 * p.N + 2 * 4 * (p.N // 4) + 4 * p.B * p.H * p.bridge_k
+        assert step >= win_min
+        # coarse steps: pooled K and V at the ramp's smallest factor, then the coarse workspace
+        f_small = min(A.area_step_info(p, s)["f"] for s in range(wl.p1_steps))
+        pooled = 2 * p.B * p.H * (p.N // f_small ** 2) * p.D * 2
+        assert step >= pooled + A.area_workspace_bytes(p, A.OP_COARSE)
+    # a canvas at or below native keeps full attention: the step needs the full workspace
+    g = prob("tiny-32", native_h=32, native_w=32)
+    assert A.area_workspace_bytes(g, A.OP_STEP) == A.area_workspace_bytes(g, A.OP_FULL)
+
+
+def test_step_rejects_bad_arguments_before_launch():
+    L = A.lib()
+    p = prob("flux-2048").c()
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    # NULL q, step out of range, latent with C < 1, workspace missing / too small
+    assert L.area_attn_step(ctypes.byref(p), 0, 0, None, None, fake, fake, fake, fake, big, None) == -1
+    assert L.area_attn_step(ctypes.byref(p), 10 ** 6, 0, None, fake, fake, fake, fake, fake, big, None) == -1
+    assert L.area_attn_step(ctypes.byref(p), 0, 0, fake, fake, fake, fake, fake, fake, big, None) == -1
+    assert L.area_attn_step(ctypes.byref(p), 0, 0, None, fake, fake, fake, fake, None, big, None) == -4
+    assert L.area_attn_step(ctypes.byref(p), 9, 16, fake, fake, fake, fake, fake, fake, 64, None) == -4
