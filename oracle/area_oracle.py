@@ -24,7 +24,7 @@ Sources (page titles, sections):
             repository layout.
 
 Where the pages leave a step open, the reading taken is marked READING and
-named (R1...R16); each is one small function here.
+named (R1...R19); each is one small function here.
 """
 from __future__ import annotations
 
@@ -234,6 +234,25 @@ def window_sizes(w_start: int, w_min: int, steps: int) -> List[int]:
     return out
 
 
+def w_start_auto(Gh: int, Gw: int, w_min: int) -> int:
+    """READING R7 of the first Phase II window ([summary] Phase II: the
+    largest window for which windowed attention is still cheaper than a
+    full-attention pass, about 70% of the longer side; [blog] Fase II, same
+    rule): the largest even w in [w_min, max(Gh, Gw)] whose base tiling
+    costs fewer (query, key) pairs than full attention, each window attending
+    to itself: sum over the R8 windows of (min(w, Gh) * min(w, Gw))^2 <
+    (Gh * Gw)^2.  w_min when no larger size qualifies."""
+    N = Gh * Gw
+    best = w_min
+    for w in range(w_min, max(Gh, Gw) + 1):
+        if w % 2:
+            continue
+        n = len(base_starts(Gh, w)) * len(base_starts(Gw, w))
+        if n * (min(w, Gh) * min(w, Gw)) ** 2 < N * N:
+            best = w
+    return best
+
+
 # ----------------------------------------------------------------------------
 # Window tiling
 # ----------------------------------------------------------------------------
@@ -404,6 +423,31 @@ def halo_rect(y0, x0, h, w, delta, Gh, Gw):
     return ky0, kx0, ky1 - ky0, kx1 - kx0
 
 
+HALO_STREAM = 0x48414C4F  # "HALO": Halo widths use their own SplitMix64 stream
+
+
+def halo_width(seed: int, step: int, base: int, quadrant: int, halo_max: int) -> int:
+    """READING R18 of the randomised Halo ([blog] Fase II: a Halo of up to
+    delta_max = 8 patches; [blog] "Cómo entra en tu pipeline": the seed
+    controls the Halo widths; [summary] Phase II: delta_max set to 8): every
+    window of every step (a quadrant is a window of its own) draws its width
+    uniformly from 1..halo_max, as
+    1 + splitmix64(seed ^ HALO_STREAM, 1 + (step * 4096 + base) * 5 + quadrant + 1) mod halo_max,
+    with base the row-major index of its base window and quadrant -1 for an
+    unsplit window."""
+    k = 1 + (step * 4096 + base) * 5 + (quadrant + 1)
+    return 1 + int(splitmix64(seed ^ HALO_STREAM, k) % halo_max)
+
+
+def bridge_size(w: int, rho_num: int, rho_den: int) -> int:
+    """READING R19 ([summary] Phase II: each window gains R = (rho w_t)^2
+    bridge tokens, rho = 0.5; [blog] Fase II, same): R_t = round_half_up(rho *
+    w_t)^2 with w_t the step's scheduled window side (one bridge set per step,
+    shared by its windows and quadrants)."""
+    side = (2 * rho_num * w + rho_den) // (2 * rho_den)
+    return side * side
+
+
 def tent(L: int) -> np.ndarray:
     """READING R15: centre weight along one axis, min(u + 1, L - u)."""
     u = np.arange(L)
@@ -411,7 +455,8 @@ def tent(L: int) -> np.ndarray:
 
 
 def window_plan(Gh: int, Gw: int, w: int, halo: int, seed: int, step: int,
-                Eq: Optional[np.ndarray], split_num: int = 1, split_den: int = 2) -> Plan:
+                Eq: Optional[np.ndarray], split_num: int = 1, split_den: int = 2,
+                halo_max: int = 0) -> Plan:
     """Phase II window list for one step ([summary] Phase II; [readme]
     repository layout: tiling covers base tiling, DWT map, splits, Halo and
     merge weights).
@@ -420,8 +465,9 @@ def window_plan(Gh: int, Gw: int, w: int, halo: int, seed: int, step: int,
     mean detail is below split_num/split_den of the grid's mean detail is
     replaced in place by its four quadrants TL, TR, BL, BR (READING R12:
     split iff den * S_w * N < num * S_tot * |Q_w| with S the integer sums of
-    E_q over tokens).  Each window then gets its Halo rectangle and its tent
-    weights accumulate into wsum."""
+    E_q over tokens).  Each window then gets its Halo rectangle (width
+    `halo`, or a seeded width per window from halo_width when halo_max > 0)
+    and its tent weights accumulate into wsum."""
     N = Gh * Gw
     ys, oy = axis_windows(Gh, w, seed, step, 0)
     xs, ox = axis_windows(Gw, w, seed, step, 1)
@@ -438,7 +484,8 @@ def window_plan(Gh: int, Gw: int, w: int, halo: int, seed: int, step: int,
                     rects = [(y0, x0, h1, w1, 0), (y0, x0 + w1, h1, wd - w1, 1),
                              (y0 + h1, x0, h - h1, w1, 2), (y0 + h1, x0 + w1, h - h1, wd - w1, 3)]
             for (ry, rx, rh, rw, quad) in rects:
-                ky0, kx0, kh, kw = halo_rect(ry, rx, rh, rw, halo, Gh, Gw)
+                delta = halo_width(seed, step, parent, quad, halo_max) if halo_max > 0 else halo
+                ky0, kx0, kh, kw = halo_rect(ry, rx, rh, rw, delta, Gh, Gw)
                 plan.windows.append(Window(ry, rx, rh, rw, ky0, kx0, kh, kw, parent, quad))
             parent += 1
     wsum = np.zeros((Gh, Gw), dtype=np.int64)

@@ -252,6 +252,75 @@ def test_w_start_rule_is_about_seventy_percent():
         assert g["fraction_low"] <= wmax / G <= g["fraction_high"], (G, wmax)
 
 
+def test_w_start_auto_closed_form_on_square_grids():
+    # On a G x G grid the R8 tiling has ceil(G/w)^2 windows of w^2 tokens (w < G), so the
+    # rule "cheaper than one full pass" is ceil(G/w)^2 * w^4 < G^4; the largest even such w
+    # is the first window, about 70% of the side for the configured grids.
+    for G in (64, 128, 256, 384, 512):
+        want = max(w for w in range(2, G, 2) if math.ceil(G / w) ** 2 * w ** 4 < G ** 4)
+        assert O.w_start_auto(G, G, 8) == want
+        if G >= 128:   # the configured grids; even sizes are coarser on small grids
+            assert 0.69 <= want / G <= 0.71
+    assert [O.w_start_auto(G, G, 8) for G in (128, 256, 384)] == [90, 180, 270]
+
+
+def test_w_start_auto_counts_pairs_of_the_actual_tiling():
+    # a non-square grid: enumerate the step's windows (no Halo, no splits) and count
+    # (query, key) pairs directly; the chosen w passes, the next even size does not.
+    Gh, Gw = 384, 128
+    w = O.w_start_auto(Gh, Gw, 64)
+
+    def pairs(ws):
+        plan = O.window_plan(Gh, Gw, ws, 0, 0, 0, None)
+        return sum(win.qh * win.qw * win.kh * win.kw for win in plan.windows)
+
+    assert pairs(w) < (Gh * Gw) ** 2 <= pairs(w + 2)
+    assert w == 270   # the longer side's 70%
+    # a minimum above every qualifying size is kept
+    assert O.w_start_auto(64, 64, 64) == 64
+
+
+def test_halo_widths_seeded_uniform_in_range():
+    draws = [O.halo_width(3, t, b, q, 8) for t in range(20) for b in range(60) for q in range(-1, 4)]
+    assert min(draws) == 1 and max(draws) == 8
+    counts = np.bincount(draws, minlength=9)[1:]
+    exp = len(draws) / 8
+    assert np.all(np.abs(counts - exp) < 0.15 * exp), counts
+    # deterministic, and a different seed gives a different sequence
+    assert draws == [O.halo_width(3, t, b, q, 8) for t in range(20) for b in range(60) for q in range(-1, 4)]
+    assert draws != [O.halo_width(4, t, b, q, 8) for t in range(20) for b in range(60) for q in range(-1, 4)]
+    # its own stream: not the jitter draws of the same seed
+    assert O.halo_width(0, 0, 0, -1, 1 << 30) - 1 != O.splitmix64(0, 1) % (1 << 30)
+
+
+def test_random_halo_rects():
+    wl = W.get("tiny-32")
+    Eq = O.energy_fixed(O.detail_energy(W.make_latent(wl)))
+    for step, w in enumerate([16, 12, 10, 8]):
+        plan = O.window_plan(wl.Gh, wl.Gw, w, 0, 11, step, Eq, halo_max=8)
+        widths = set()
+        for win in plan.windows:
+            d = O.halo_width(11, step, win.parent, win.quadrant, 8)
+            widths.add(d)
+            assert 1 <= d <= 8
+            assert (win.ky0, win.kx0, win.kh, win.kw) == O.halo_rect(win.qy0, win.qx0, win.qh, win.qw, d,
+                                                                     wl.Gh, wl.Gw)
+        if len(plan.windows) > 4:
+            assert len(widths) > 1
+        # delta_max = 1 is the fixed Halo of width 1
+        fixed = O.window_plan(wl.Gh, wl.Gw, w, 1, 11, step, Eq)
+        one = O.window_plan(wl.Gh, wl.Gw, w, 0, 11, step, Eq, halo_max=1)
+        np.testing.assert_array_equal(fixed.records(), one.records())
+
+
+def test_bridge_size_per_step():
+    for w in range(2, 400, 2):
+        assert O.bridge_size(w, 1, 2) == (w // 2) ** 2          # rho = 0.5 on even sides
+    assert O.bridge_size(192, 1, 2) == 9216 and O.bridge_size(64, 1, 2) == 1024
+    assert O.bridge_size(5, 1, 2) == 9                           # round half up: 2.5 -> 3
+    assert O.bridge_size(10, 1, 3) == 9                          # 3.33 -> 3
+
+
 def test_base_tiling_properties():
     for G in range(8, 70):
         for w in range(2, G + 3):
