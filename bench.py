@@ -14,8 +14,10 @@ warm-up steps with inputs already resident in HBM.  Prints one JSON line.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--ablation]
 
 --ablation prints, instead of the bench line, the schedule's time with the
-quadrant splits, the Halo or the bridge turned off, and at a fixed smallest
-window, each against the same full-attention baseline.
+quadrant splits, the Halo or the bridge turned off, at a fixed smallest
+window, and at the pages' own knob values (first window from the cost rule,
+seeded Halo widths up to 8, bridge of (w/2)^2 tokens), each against the same
+full-attention baseline.
 """
 from __future__ import annotations
 
@@ -80,14 +82,22 @@ class Schedule:
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.plan = torch.zeros(A.area_plan_words(p), dtype=torch.int32, device=dev)
         self.wsum = torch.empty(N, dtype=torch.int32, device=dev)
-        self.bridge = (torch.empty((B, H, p.bridge_k), dtype=torch.int32, device=dev) if p.bridge_k > 0 else None)
-        self.energy = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.float32, device=dev)
-        self.energy_q = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.int32, device=dev)
         self.n_steps = p.p1_steps + p.p2_steps
         self.sched = [A.area_step_info(p, s) for s in range(self.n_steps)]
+        r_max = max([st["R"] for st in self.sched] + [0])
+        self.bridge_buf = torch.empty(B * H * r_max, dtype=torch.int32, device=dev) if r_max > 0 else None
+        self.energy = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.float32, device=dev)
+        self.energy_q = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.int32, device=dev)
         fs = sorted({st["f"] for st in self.sched if st["phase"] == A.PHASE_COARSE})
         self.kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev),
                         torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev)) for f in fs}
+
+    def bridge(self, s):
+        """The step's bridge-index view [B, H, R_s] of the shared buffer (None without a bridge)."""
+        R = self.sched[s]["R"]
+        if R == 0 or self.bridge_buf is None:
+            return None
+        return self.bridge_buf[:self.p.B * self.p.H * R].view(self.p.B, self.p.H, R)
 
     @staticmethod
     def _tev():
@@ -99,7 +109,7 @@ class Schedule:
     def window_plan(self, s):
         A, p = self.A, self.p
         A.area_dwt_detail(p, self.lat, self.energy, self.energy_q)
-        A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, self.bridge, self.ws)
+        A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, self.bridge(s), self.ws)
 
     def one_pass(self, rec, full=True):
         """Enqueue the whole hot path once; rec collects (kind, step, events)."""
@@ -121,11 +131,12 @@ class Schedule:
                 e0 = tev()
                 A.area_dwt_detail(p, self.lat, self.energy, self.energy_q)
                 e1 = tev()
-                A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, self.bridge, self.ws)
+                br = self.bridge(s)
+                A.area_window_plan(p, s, self.energy_q, self.k, self.plan, self.wsum, br, self.ws)
                 e2 = tev()
                 a0, a1 = ev.new(), ev.new()
                 A.area_set_attn_events(a0, a1)
-                A.area_window_attn(p, s, self.plan, self.wsum, self.bridge, self.q, self.k, self.v, self.out, self.ws)
+                A.area_window_attn(p, s, self.plan, self.wsum, br, self.q, self.k, self.v, self.out, self.ws)
                 A.area_set_attn_events(None, None)
                 e3 = tev()
                 rec.append(("window", s, (e0, e1, e2, e3, a0, a1)))
@@ -152,14 +163,15 @@ class Schedule:
             pl = self.plan.cpu().numpy()
             nwin = int(pl[0])
             recs = pl[A.PLAN_HEADER:A.PLAN_HEADER + A.PLAN_REC * nwin].reshape(nwin, A.PLAN_REC)
-            if self.bridge is not None:
-                br = self.bridge.cpu().numpy().reshape(BH, -1)
+            brt = self.bridge(s)
+            if brt is not None:
+                br = brt.cpu().numpy().reshape(BH, -1)
                 by, bx = br // Gw, br % Gw
             pairs = 0
             for r in recs:
                 qy0, qx0, qh, qw, ky0, kx0, kh, kw = (int(x) for x in r[:8])
                 nkv = kh * kw * BH
-                if self.bridge is not None:
+                if brt is not None:
                     inside = (by >= ky0) & (by < ky0 + kh) & (bx >= kx0) & (bx < kx0 + kw)
                     nkv += int((~inside).sum())
                 pairs += qh * qw * nkv
@@ -355,11 +367,14 @@ def main():
 
 def run_ablation(A, wl, base, args):
     """Attention-time ablations of the AReA schedule (quadrant splits off,
-    Halo off, bridge off, fixed smallest window), each against the same
-    full-attention baseline; prints one JSON line."""
+    Halo off, bridge off, fixed smallest window) and the pages' own knob
+    values, each against the same full-attention baseline; prints one JSON
+    line."""
     import torch
+    import workloads as W
     variants = [("as configured", {}), ("no quadrant splits", {"split_num": 0}), ("no halo", {"halo": 0}),
-                ("no bridge", {"bridge_k": 0}), (f"fixed w={wl.w_min}", {"w_start": wl.w_min})]
+                ("no bridge", {"bridge_k": 0}), (f"fixed w={wl.w_min}", {"w_start": wl.w_min}),
+                ("pages' knobs (w_start rule, seeded Halo <= 8, bridge (w/2)^2)", dict(W.PAGES_KNOBS))]
     rows = []
     full_ms = None
     for name, over in variants:

@@ -87,7 +87,7 @@ extern "C" {
 #define AREA_PH_NX     4       /* base windows along x                          */
 #define AREA_PH_JITY   5       /* boundary shift applied along y                */
 #define AREA_PH_JITX   6       /* boundary shift applied along x                */
-#define AREA_PH_HALO   7       /* Halo width                                    */
+#define AREA_PH_HALO   7       /* Halo width (its maximum when drawn per window) */
 #define AREA_PH_R      8       /* bridge tokens per (batch, head); 0 = none     */
 #define AREA_PH_NSPLIT 9       /* base windows that were split                  */
 #define AREA_PH_QTOT  10       /* sum of query-rect areas over all windows      */
@@ -105,11 +105,20 @@ typedef struct area_problem {
   int32_t f_min;              /* pooling floor (2)                               */
   int32_t pool_mode;          /* AREA_POOL_MEAN | AREA_POOL_CENTER               */
   int32_t p2_steps;           /* Phase II (window) steps                         */
-  int32_t w_start, w_min;     /* window side at the first / last Phase II step   */
-  int32_t halo;               /* Halo width in tokens                            */
-  int32_t bridge_k;           /* bridge tokens per (batch, head); 0 = no bridge  */
+  int32_t w_start, w_min;     /* window side at the first / last Phase II step;  */
+                              /* w_start 0 = derive (largest even side whose     */
+                              /* tiling costs fewer pairs than full attention)   */
+  int32_t halo;               /* Halo width in tokens (when halo_max == 0)       */
+  int32_t bridge_k;           /* bridge tokens per (batch, head) when            */
+                              /* bridge_rho_num == 0; 0 = no bridge              */
   int32_t split_num, split_den; /* smooth-window threshold (1/2)                 */
-  uint64_t seed;              /* seeds the per-step window-boundary shift        */
+  uint64_t seed;              /* seeds the window-boundary shift and the Halo    */
+                              /* widths                                          */
+  int32_t halo_max;           /* > 0: every window draws its Halo width from     */
+                              /* 1..halo_max (seeded); 0: fixed width `halo`     */
+  int32_t bridge_rho_num, bridge_rho_den; /* num > 0: the bridge of window step  */
+                              /* t has R_t = round(rho w_t)^2 tokens, rho =      */
+                              /* num/den; 0: bridge_k at every step              */
 } area_problem;
 
 typedef struct area_step {
@@ -120,6 +129,8 @@ typedef struct area_step {
   int32_t jit_y, jit_x;       /* boundary shift per axis                         */
   int32_t max_windows;        /* upper bound on windows after splits (4 ny nx)   */
   int64_t q_total;            /* sum of base-window query areas                  */
+  int32_t R;                  /* bridge tokens per (batch, head) of a window     */
+                              /* step (0: none), else 0                          */
 } area_step;
 
 /* ---- host-only calls (no GPU needed) ------------------------------------ */
@@ -216,10 +227,16 @@ int area_dwt_detail(const area_problem* p, int C, const float* latent, float* en
  *          query rectangle dilated by the Halo and clipped to the grid.
  *  wsum:   [Gh*Gw] int32, sum over covering windows of the tent weight
  *          min(u+1, L-u) along y times along x.
- *  bridge_idx: [B][H][bridge_k] int32 sorted ascending: per (b, h), the key
+ *          The Halo width is p->halo, or, with p->halo_max > 0, drawn per
+ *          window from 1..halo_max: 1 + splitmix64(seed ^ 0x48414C4F,
+ *          1 + (t * 4096 + parent) * 5 + quadrant + 1) mod halo_max, t the
+ *          Phase II step index, parent the base-window index, quadrant -1
+ *          for an unsplit window.
+ *  bridge_idx: [B][H][R] int32 sorted ascending, R = area_step_info().R of
+ *          the step (p->bridge_k, or round(rho w_t)^2): per (b, h), the key
  *          farthest (sum of squared channel deviations, float64, channels in
- *          order) from the exact mean key in each of bridge_k cells of a
- *          r_h x r_w grid of the image; ties to the smaller index.
+ *          order) from the exact mean key in each of R cells of a r_h x r_w
+ *          grid of the image; ties to the smaller index.
  * Workspace: area_workspace_bytes(p, AREA_OP_PLAN). */
 int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, const void* k,
                      int32_t* plan, int32_t* wsum, int32_t* bridge_idx,

@@ -50,14 +50,16 @@ class _Problem(ctypes.Structure):
                 ("pool_mode", ctypes.c_int32), ("p2_steps", ctypes.c_int32),
                 ("w_start", ctypes.c_int32), ("w_min", ctypes.c_int32), ("halo", ctypes.c_int32),
                 ("bridge_k", ctypes.c_int32), ("split_num", ctypes.c_int32),
-                ("split_den", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("split_den", ctypes.c_int32), ("seed", ctypes.c_uint64),
+                ("halo_max", ctypes.c_int32), ("bridge_rho_num", ctypes.c_int32),
+                ("bridge_rho_den", ctypes.c_int32)]
 
 
 class _Step(ctypes.Structure):
     _fields_ = [("phase", ctypes.c_int32), ("f", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("ny", ctypes.c_int32), ("nx", ctypes.c_int32), ("jit_y", ctypes.c_int32),
                 ("jit_x", ctypes.c_int32), ("max_windows", ctypes.c_int32),
-                ("q_total", ctypes.c_int64)]
+                ("q_total", ctypes.c_int64), ("R", ctypes.c_int32)]
 
 
 @dataclass
@@ -84,12 +86,16 @@ class Problem:
     split_num: int = 1
     split_den: int = 2
     seed: int = 0
+    halo_max: int = 0
+    bridge_rho_num: int = 0
+    bridge_rho_den: int = 1
 
     def c(self) -> _Problem:
         return _Problem(self.B, self.H, self.D, self.Gh, self.Gw, self.native_h, self.native_w,
                         self.T, self.rope_theta, self.p1_steps, self.f0, self.f_min, self.pool_mode,
                         self.p2_steps, self.w_start, self.w_min, self.halo, self.bridge_k,
-                        self.split_num, self.split_den, self.seed & ((1 << 64) - 1))
+                        self.split_num, self.split_den, self.seed & ((1 << 64) - 1),
+                        self.halo_max, self.bridge_rho_num, self.bridge_rho_den)
 
     @property
     def N(self) -> int:
@@ -293,13 +299,14 @@ def area_window_plan(p: Problem, step: int, energy_q, k, plan=None, wsum=None, b
     words = area_plan_words(p)
     plan = torch.zeros(words, dtype=torch.int32, device=dev) if plan is None else plan
     wsum = torch.empty(p.N, dtype=torch.int32, device=dev) if wsum is None else wsum
-    use_bridge = k is not None and p.bridge_k > 0
+    R = area_step_info(p, step)["R"]
+    use_bridge = k is not None and R > 0
     if use_bridge and bridge_idx is None:
-        bridge_idx = torch.empty((p.B, p.H, p.bridge_k), dtype=torch.int32, device=dev)
+        bridge_idx = torch.empty((p.B, p.H, R), dtype=torch.int32, device=dev)
     _need(plan, torch.int32, (words,), "plan")
     _need(wsum, torch.int32, (p.N,), "wsum")
     if use_bridge:
-        _need(bridge_idx, torch.int32, (p.B, p.H, p.bridge_k), "bridge_idx")
+        _need(bridge_idx, torch.int32, (p.B, p.H, R), "bridge_idx")
     ws = workspace(p, OP_PLAN, dev) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_window_plan(ref, step, _ptr(energy_q), _ptr(k), _ptr(plan), _ptr(wsum),
@@ -316,7 +323,7 @@ def area_window_attn(p: Problem, step: int, plan, wsum, bridge_idx, q, k, v, out
     _need(plan, torch.int32, (area_plan_words(p),), "plan")
     _need(wsum, torch.int32, (p.N,), "wsum")
     if bridge_idx is not None:
-        _need(bridge_idx, torch.int32, (p.B, p.H, p.bridge_k), "bridge_idx")
+        _need(bridge_idx, torch.int32, (p.B, p.H, area_step_info(p, step)["R"]), "bridge_idx")
     out = torch.empty_like(q) if out is None else out
     _need(out, torch.bfloat16, shp, "out")
     ws = workspace(p, OP_WINDOW, q.device) if ws is None else ws

@@ -75,22 +75,6 @@ int ramp_factor(const area_problem& p, int f0, int t) {
   return nearest_common_divisor(p.Gh, p.Gw, p.f_min, num, den);
 }
 
-// READING R6 (ai.info summary, Methodology, Phase II: geometric shrink from
-// w_start to w_min): r_t = w_start (w_min / w_start)^(t / (S - 1)) in
-// float64, then the nearest even integer, ties up.
-int window_side(const area_problem& p, int t) {
-  int S = p.p2_steps;
-  double r;
-  if (S <= 1) {
-    r = (double)p.w_start;
-  } else {
-    double ratio = (double)p.w_min / (double)p.w_start;
-    double e = (double)t / (double)(S - 1);
-    r = (double)p.w_start * std::pow(ratio, e);
-  }
-  return 2 * (int)std::floor(r / 2.0 + 0.5);
-}
-
 // READING R8 (ai.info summary, Phase II: evenly spaced base tiling):
 // n = ceil(G / w) windows (1 if w >= G), b_i = round_half_up(i (G-w)/(n-1)).
 void base_starts(int G, int w, std::vector<int>& out) {
@@ -102,6 +86,54 @@ void base_starts(int G, int w, std::vector<int>& out) {
   int n = (G + w - 1) / w;
   for (int i = 0; i < n; ++i)
     out.push_back((int)((2LL * i * (G - w) + (n - 1)) / (2LL * (n - 1))));
+}
+
+static int64_t axis_count(int G, int w) { return w >= G ? 1 : (G + w - 1) / w; }
+
+// READING R7 (ai.info summary, Methodology, Phase II; blog, Fase II: the
+// first window is the largest for which windowed attention is still cheaper
+// than one full-attention pass, about 70% of the longer side): with
+// p.w_start == 0, the largest even w in [w_min, max(Gh, Gw)] whose base
+// tiling, each window attending to itself, has fewer (query, key) pairs than
+// full attention: n_y n_x (min(w,Gh) min(w,Gw))^2 < (Gh Gw)^2, compared in
+// 128-bit integers; w_min when nothing larger qualifies.
+int w_start_of(const area_problem& p) {
+  if (p.w_start > 0) return p.w_start;
+  const unsigned __int128 N = (unsigned __int128)p.Gh * p.Gw;
+  int best = p.w_min;
+  for (int w = p.w_min; w <= std::max(p.Gh, p.Gw); ++w) {
+    if (w % 2) continue;
+    const unsigned __int128 area = (unsigned __int128)std::min(w, p.Gh) * std::min(w, p.Gw);
+    const unsigned __int128 n = (unsigned __int128)axis_count(p.Gh, w) * axis_count(p.Gw, w);
+    if (n * area * area < N * N) best = w;
+  }
+  return best;
+}
+
+// READING R6 (ai.info summary, Methodology, Phase II: geometric shrink from
+// w_start to w_min): r_t = w_start (w_min / w_start)^(t / (S - 1)) in
+// float64, then the nearest even integer, ties up.
+int window_side(const area_problem& p, int t) {
+  int S = p.p2_steps;
+  const int w0 = w_start_of(p);
+  double r;
+  if (S <= 1) {
+    r = (double)w0;
+  } else {
+    double ratio = (double)p.w_min / (double)w0;
+    double e = (double)t / (double)(S - 1);
+    r = (double)w0 * std::pow(ratio, e);
+  }
+  return 2 * (int)std::floor(r / 2.0 + 0.5);
+}
+
+// READING R19 (ai.info summary, Phase II; blog, Fase II: each window of side
+// w gains (rho w)^2 bridge tokens, rho = 0.5): with bridge_rho_num > 0 the
+// step's bridge has round_half_up(rho w_t)^2 tokens, else bridge_k.
+int bridge_size(const area_problem& p, int w) {
+  if (p.bridge_rho_num <= 0) return p.bridge_k;
+  const long long side = (2LL * p.bridge_rho_num * w + p.bridge_rho_den) / (2LL * p.bridge_rho_den);
+  return (int)std::min<long long>(side * side, 1LL << 30);
 }
 
 // SplitMix64 (Steele, Lea, Flood 2014): k-th output from state `seed`.
@@ -177,11 +209,13 @@ int window_step(const area_problem& p, int step, WindowStepInfo& out) {
   int64_t split = ceil_div(h1 * w1, kAttnBM) + ceil_div(h1 * (Lx - w1), kAttnBM) +
                   ceil_div((Ly - h1) * w1, kAttnBM) + ceil_div((Ly - h1) * (Lx - w1), kAttnBM);
   out.max_items = nb * (unsplit > split ? unsplit : split);
-  // gathered key tiles: Halo rectangle (clipped to the grid) + all R bridge
-  // slots per window, rounded up to 64 keys
-  int64_t R = p.bridge_k;
-  int64_t kh = std::min<int64_t>(Ly + 2 * p.halo, p.Gh), kw = std::min<int64_t>(Lx + 2 * p.halo, p.Gw);
-  int64_t qh = std::min<int64_t>(Ly - h1 + 2 * p.halo, p.Gh), qw = std::min<int64_t>(Lx - w1 + 2 * p.halo, p.Gw);
+  // gathered key tiles: Halo rectangle (clipped to the grid, widest Halo) +
+  // all R bridge slots per window, rounded up to 64 keys
+  out.R = bridge_size(p, out.w);
+  int64_t R = out.R;
+  int64_t hw = p.halo_max > 0 ? p.halo_max : p.halo;
+  int64_t kh = std::min<int64_t>(Ly + 2 * hw, p.Gh), kw = std::min<int64_t>(Lx + 2 * hw, p.Gw);
+  int64_t qh = std::min<int64_t>(Ly - h1 + 2 * hw, p.Gh), qw = std::min<int64_t>(Lx - w1 + 2 * hw, p.Gw);
   int64_t g_unsplit = ceil_div(kh * kw + R, kAttnBN);
   int64_t g_split = 4 * ceil_div(qh * qw + R, kAttnBN);
   out.max_gtiles = nb * (g_unsplit > g_split ? g_unsplit : g_split);
@@ -203,7 +237,10 @@ static int validate(const area_problem* pp) {
   if (p.pool_mode != AREA_POOL_MEAN && p.pool_mode != AREA_POOL_CENTER)
     return fail(AREA_E_INVALID, pstr("pool_mode", p.pool_mode));
   if (p.f_min < 1 || p.f0 < 0) return fail(AREA_E_INVALID, "f_min must be >= 1 and f0 >= 0");
-  if (p.halo < 0 || p.bridge_k < 0) return fail(AREA_E_INVALID, "halo and bridge_k must be >= 0");
+  if (p.halo < 0 || p.bridge_k < 0 || p.halo_max < 0)
+    return fail(AREA_E_INVALID, "halo, halo_max and bridge_k must be >= 0");
+  if (p.bridge_rho_num < 0 || (p.bridge_rho_num > 0 && p.bridge_rho_den <= 0))
+    return fail(AREA_E_INVALID, "bridge_rho_num >= 0, and bridge_rho_den > 0 when it is used");
   if (p.split_den <= 0 || p.split_num < 0) return fail(AREA_E_INVALID, "split_num >= 0, split_den > 0");
   long long N = (long long)p.Gh * p.Gw;
   if (N > (1LL << 30) || (long long)p.B * p.H * N * p.D > (1LL << 40))
@@ -217,16 +254,18 @@ static int validate(const area_problem* pp) {
     return fail(AREA_E_SHAPE, pstr("f0 must be a common grid divisor >= f_min, f0", p.f0));
   if (p.f0 == 0 && derive_f0(p) < 0) return fail(AREA_E_SHAPE, "no pooling factor fits the grid");
   if (p.p2_steps > 0) {
-    if (p.w_min < 2 || p.w_start < p.w_min || p.w_min % 2 || p.w_start % 2)
-      return fail(AREA_E_SHAPE, "window sides must be even with 2 <= w_min <= w_start");
+    if (p.w_min < 2 || p.w_min % 2 || (p.w_start != 0 && (p.w_start < p.w_min || p.w_start % 2)))
+      return fail(AREA_E_SHAPE, "window sides must be even with 2 <= w_min <= w_start (w_start 0: derived)");
     int nmax_y = (p.Gh + p.w_min - 1) / p.w_min, nmax_x = (p.Gw + p.w_min - 1) / p.w_min;
     if (nmax_y > kMaxAxisWindows || nmax_x > kMaxAxisWindows)
       return fail(AREA_E_UNSUPPORTED, "w_min gives more than 64 base windows per axis");
-    if (p.bridge_k > 0) {
+    for (int t = 0; t < p.p2_steps; ++t) {
+      const int R = bridge_size(p, window_side(p, t));
+      if (R <= 0) continue;
       int rh, rw;
-      if (!bridge_cells(p.bridge_k, p.Gh, p.Gw, rh, rw))
-        return fail(AREA_E_SHAPE, pstr("bridge cells do not fit the grid, bridge_k", p.bridge_k));
-      if (p.bridge_k > 4096) return fail(AREA_E_UNSUPPORTED, "bridge_k above 4096");
+      if (!bridge_cells(R, p.Gh, p.Gw, rh, rw))
+        return fail(AREA_E_SHAPE, pstr("bridge cells do not fit the grid, R", R));
+      if (rw > kBridgeSortMax) return fail(AREA_E_UNSUPPORTED, pstr("bridge cell rows above 4096 cells, R", R));
     }
   }
   return AREA_OK;
@@ -238,7 +277,7 @@ static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * N_of(
 
 struct WindowMax {
   int64_t q_total = 0, max_items = 0, max_gtiles = 0;
-  int max_windows = 0, n_base = 0;
+  int max_windows = 0, n_base = 0, max_R = 0;
 };
 
 static WindowMax window_max(const area_problem& p) {
@@ -252,6 +291,7 @@ static WindowMax window_max(const area_problem& p) {
     m.max_gtiles = std::max<int64_t>(m.max_gtiles, wi.max_gtiles);
     m.max_windows = std::max(m.max_windows, 4 * nb);
     m.n_base = std::max(m.n_base, nb);
+    m.max_R = std::max(m.max_R, wi.R);
   }
   return m;
 }
@@ -277,7 +317,7 @@ static WindowLayout window_layout(const area_problem& p) {
   l.items = take(window_items_ws_bytes(m.max_windows, m.max_items, m.n_base, m.max_gtiles));
   l.kg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
   l.vg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
-  l.blist = take((size_t)m.max_windows * BH * std::max(p.bridge_k, 1) * 4);
+  l.blist = take((size_t)m.max_windows * BH * std::max(m.max_R, 1) * 4);
   l.bcount = take((size_t)m.max_windows * BH * 4);
   l.total = off;
   return l;
@@ -327,7 +367,7 @@ static StepLayout step_layout(const area_problem& p) {
     l.wsum = o;
     o += align_up(N * 4);
     l.bridge = o;
-    o += align_up(BH * std::max(p.bridge_k, 1) * 4);
+    o += align_up(BH * std::max(window_max(p).max_R, 1) * 4);
     l.window_ws = o;
     window = o + std::max(workspace_bytes(p, AREA_OP_PLAN), workspace_bytes(p, AREA_OP_WINDOW));
   }
@@ -347,7 +387,7 @@ static size_t workspace_bytes(const area_problem& p, int op) {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
       WindowMax m = window_max(p);
       return align_up(plan_ws_bytes(m.n_base)) +
-             align_up(bridge_ws_bytes(BH_of(p), (int)N_of(p), p.D, p.bridge_k));
+             align_up(bridge_ws_bytes(BH_of(p), (int)N_of(p), p.D, m.max_R));
     }
     case AREA_OP_WINDOW: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
@@ -412,6 +452,7 @@ int area_step_info(const area_problem* p, int step, area_step* out) {
   out->jit_x = wi.tx.jitter;
   out->max_windows = 4 * wi.ty.n * wi.tx.n;
   out->q_total = wi.q_total;
+  out->R = wi.R;
   return AREA_OK;
 }
 
@@ -535,7 +576,7 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
   rc = window_step(*p, step, wi);
   if (rc) return rc;
   if (!plan || !wsum) return fail(AREA_E_INVALID, "NULL plan or wsum");
-  bool use_bridge = p->bridge_k > 0 && k != nullptr;
+  bool use_bridge = wi.R > 0 && k != nullptr;
   if (use_bridge && !bridge_idx) return fail(AREA_E_INVALID, "bridge_idx is NULL");
   rc = check_ws(*p, AREA_OP_PLAN, ws, ws_bytes);
   if (rc) return rc;
@@ -543,8 +584,10 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
   std::memset(&a, 0, sizeof(a));
   a.Gh = p->Gh;
   a.Gw = p->Gw;
-  a.halo = p->halo;
-  a.R = use_bridge ? p->bridge_k : 0;
+  a.halo = p->halo_max > 0 ? p->halo_max : p->halo;
+  a.halo_max = p->halo_max;
+  a.seed = p->seed;
+  a.R = use_bridge ? wi.R : 0;
   a.split_num = p->split_num;
   a.split_den = energy_q ? p->split_den : 0;  // 0: never split
   a.t = wi.t;
@@ -563,8 +606,8 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
   if (rc) return rc;
   if (use_bridge) {
     int rh, rw;
-    bridge_cells(p->bridge_k, p->Gh, p->Gw, rh, rw);
-    rc = launch_bridge(k, bridge_idx, BH_of(*p), p->Gh, p->Gw, p->D, p->bridge_k, rh, rw,
+    bridge_cells(wi.R, p->Gh, p->Gw, rh, rw);
+    rc = launch_bridge(k, bridge_idx, BH_of(*p), p->Gh, p->Gw, p->D, wi.R, rh, rw,
                        wsb + align_up(plan_ws_bytes(m.n_base)), stream);
   }
   return rc;
@@ -586,7 +629,7 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   a.Gh = p->Gh;
   a.Gw = p->Gw;
   a.D = p->D;
-  a.R = (bridge_idx && p->bridge_k > 0) ? p->bridge_k : 0;
+  a.R = (bridge_idx && wi.R > 0) ? wi.R : 0;
   a.BH = BH_of(*p);
   a.max_windows = 4 * wi.ty.n * wi.tx.n;
   a.max_items = wi.max_items;
@@ -638,7 +681,7 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       int32_t* energy_q = (int32_t*)(base + l.energy_q);
       int32_t* plan = (int32_t*)(base + l.plan);
       int32_t* wsum = (int32_t*)(base + l.wsum);
-      int32_t* bridge = p->bridge_k > 0 ? (int32_t*)(base + l.bridge) : nullptr;
+      int32_t* bridge = st.R > 0 ? (int32_t*)(base + l.bridge) : nullptr;
       if (latent) {
         rc = area_dwt_detail(p, C, latent, energy, energy_q, stream);
         if (rc) return rc;

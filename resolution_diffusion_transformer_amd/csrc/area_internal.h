@@ -35,7 +35,9 @@ int gcd_int(int a, int b);
 int nearest_common_divisor(int a, int b, int lo, long long num, long long den);
 int derive_f0(const area_problem& p);              // READING R5
 int ramp_factor(const area_problem& p, int f0, int t);  // READING R4
+int w_start_of(const area_problem& p);            // READING R7
 int window_side(const area_problem& p, int t);     // READING R6
+int bridge_size(const area_problem& p, int w);     // READING R19
 void base_starts(int G, int w, std::vector<int>& out);  // READING R8
 uint64_t splitmix64(uint64_t seed, uint64_t k);
 int jitter_offset(const std::vector<int>& starts, int L, uint64_t seed, int t, int axis);  // R9
@@ -62,6 +64,7 @@ struct WindowStepInfo {
   int64_t q_total = 0;       // sum of query areas (== with splits)
   int64_t max_items = 0;     // work items (window, query tile) over all split choices
   int64_t max_gtiles = 0;    // gathered 64-key tiles over all split choices
+  int R = 0;                 // bridge tokens per (batch, head) of the step
 };
 int window_step(const area_problem& p, int step, WindowStepInfo& out);
 
@@ -88,6 +91,8 @@ int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int
 
 struct PlanArgs {
   int Gh, Gw, halo, R, split_num, split_den, t, w;
+  int halo_max;                  // > 0: per-window Halo widths drawn from 1..halo_max
+  unsigned long long seed;
   int ny, nx, jit_y, jit_x, Ly, Lx;
   int ys[kMaxAxisWindows];
   int xs[kMaxAxisWindows];
@@ -98,6 +103,7 @@ size_t plan_ws_bytes(int n_base);
 
 int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D, int R, int rh,
                   int rw, void* ws, stream_t s);
+constexpr int kBridgeSortMax = 4096;  // cells per row of the bridge cell grid
 size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
 
 // fp16 V^T tiles of 64 keys: vt[bh][t][d][k] = v[bh][64 t + k][d], zero

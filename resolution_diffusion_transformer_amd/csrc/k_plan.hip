@@ -86,6 +86,24 @@ __device__ inline bool split_test(long long Sw, long long Stot, long long N, lon
   return lhs < rhs;
 }
 
+// SplitMix64 (Steele, Lea, Flood 2014): k-th output from state `seed`.
+__device__ inline unsigned long long splitmix64_dev(unsigned long long seed, unsigned long long k) {
+  unsigned long long z = seed + k * 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// Halo width of one window: fixed, or (READING R18: the seed controls the
+// Halo widths, up to delta_max) drawn from 1..halo_max on a stream of its
+// own, keyed by step, base window and quadrant (-1 when unsplit).
+__device__ inline int halo_of(const PlanArgs& a, int base, int quadrant) {
+  if (a.halo_max <= 0) return a.halo;
+  const unsigned long long key = 1ULL + ((unsigned long long)a.t * 4096ULL + (unsigned long long)base) * 5ULL +
+                                 (unsigned long long)(quadrant + 1);
+  return 1 + (int)(splitmix64_dev(a.seed ^ 0x48414C4FULL, key) % (unsigned long long)a.halo_max);
+}
+
 // One block: split decisions, canonical record order, Halo rectangles and
 // the plan header.
 __global__ __launch_bounds__(256) void plan_emit_kernel(PlanArgs a, const long long* __restrict__ scores,
@@ -132,8 +150,9 @@ __global__ __launch_bounds__(256) void plan_emit_kernel(PlanArgs a, const long l
     }
     for (int i = 0; i < nr; ++i) {
       int ry = rects[i][0], rx = rects[i][1], rh = rects[i][2], rw = rects[i][3];
-      int ky0 = max(0, ry - a.halo), kx0 = max(0, rx - a.halo);
-      int ky1 = min(a.Gh, ry + rh + a.halo), kx1 = min(a.Gw, rx + rw + a.halo);
+      const int d = halo_of(a, b, rects[i][4]);
+      int ky0 = max(0, ry - d), kx0 = max(0, rx - d);
+      int ky1 = min(a.Gh, ry + rh + d), kx1 = min(a.Gw, rx + rw + d);
       int32_t* rec = plan + AREA_PLAN_HEADER + (int64_t)AREA_PLAN_REC * (s_first[b] + i);
       rec[0] = ry; rec[1] = rx; rec[2] = rh; rec[3] = rw;
       rec[4] = ky0; rec[5] = kx0; rec[6] = ky1 - ky0; rec[7] = kx1 - kx0;
@@ -335,13 +354,19 @@ __global__ __launch_bounds__(256) void bridge_cell_kernel(const unsigned short* 
   }
 }
 
-// Ascending sort of the R winners of one (batch*head), bitonic in LDS.
-__global__ __launch_bounds__(1024) void bridge_sort_kernel(const int* __restrict__ cell, int* __restrict__ idx, int R) {
-  __shared__ int s[4096];
-  int64_t bh = blockIdx.x;
+// Ascending order of the R winners of one (batch*head).  Cell (a, c) sits at
+// a * rw + c and cell row a covers grid rows [a Gh / rh, (a+1) Gh / rh), so
+// every winner of a cell row precedes every winner of the next: sorting each
+// row of rw cells in place (bitonic, in LDS) sorts the whole list.  One block
+// per (cell row, batch*head).
+__global__ __launch_bounds__(1024) void bridge_sort_kernel(const int* __restrict__ cell, int* __restrict__ idx,
+                                                           int rh, int rw) {
+  __shared__ int s[kBridgeSortMax];
+  const int64_t row = blockIdx.x, bh = blockIdx.y;
+  const int64_t base = bh * (int64_t)rh * rw + row * rw;
   int P = 1;
-  while (P < R) P <<= 1;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < R ? cell[bh * R + i] : 0x7FFFFFFF;
+  while (P < rw) P <<= 1;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) s[i] = i < rw ? cell[base + i] : 0x7FFFFFFF;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -359,7 +384,7 @@ __global__ __launch_bounds__(1024) void bridge_sort_kernel(const int* __restrict
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < R; i += blockDim.x) idx[bh * R + i] = s[i];
+  for (int i = threadIdx.x; i < rw; i += blockDim.x) idx[base + i] = s[i];
 }
 
 }  // namespace
@@ -418,7 +443,9 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D
                        (const double*)b.mean, b.cell, Gh, Gw, rh, rw);
   rc = check_launch("bridge_cell_kernel");
   if (rc) return rc;
-  hipLaunchKernelGGL(bridge_sort_kernel, dim3((unsigned)BH), dim3(1024), 0, st, (const int*)b.cell, idx, R);
+  if (rw > kBridgeSortMax || rh > 65535) return fail(AREA_E_UNSUPPORTED, "bridge cell grid too large");
+  hipLaunchKernelGGL(bridge_sort_kernel, dim3((unsigned)rh, (unsigned)BH), dim3(1024), 0, st, (const int*)b.cell,
+                     idx, rh, rw);
   return check_launch("bridge_sort_kernel");
 }
 

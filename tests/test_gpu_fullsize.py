@@ -265,3 +265,47 @@ def test_ablation_knobs(mid, name):
                                        br_ref[h][None, None] if R > 0 else None,
                                        wl.Gh, wl.Gw, wl.rope_theta, rows=rows)
             close(head(out, h)[:, :, rows], o_ref, f"{wl.name} ablation {name} step {t} (w={sizes[t]}) head {h}")
+
+
+# --------------------------------------------------- the pages' knob values --
+# First window from the cost rule, seeded Halo widths up to 8 per window and a
+# bridge of (w/2)^2 tokens at window side w.
+
+def test_window_steps_pages_knobs(big):
+    wl, q, k, v = big
+    p = A.problem_for(wl, **W.PAGES_KNOBS)
+    lat = W.make_latent(wl)
+    _, Eq = A.area_dwt_detail(p, torch.from_numpy(lat).cuda())
+    Eq_ref = O.energy_fixed(O.detail_energy(lat))
+    w0 = O.w_start_auto(wl.Gh, wl.Gw, wl.w_min)
+    sizes = O.window_sizes(w0, wl.w_min, wl.p2_steps)
+    heads = (0, wl.H - 3)
+    check_attn = {0, 1, wl.p2_steps - 1}
+    say(f"{wl.name}: pages' knobs, w_start {w0}, bridge {O.bridge_size(sizes[0], 1, 2)} .. "
+        f"{O.bridge_size(sizes[-1], 1, 2)}")
+    for t, w in enumerate(sizes):
+        s = wl.p1_steps + t
+        R = O.bridge_size(w, 1, 2)
+        plan, wsum, br = A.area_window_plan(p, s, Eq, k)
+        torch.cuda.synchronize()
+        ref = O.window_plan(wl.Gh, wl.Gw, w, 0, wl.seed, t, Eq_ref, halo_max=8)
+        pl = plan.cpu().numpy()
+        nwin = int(pl[0])
+        assert nwin == len(ref.windows), (wl.name, t)
+        np.testing.assert_array_equal(pl[16:16 + 10 * nwin].reshape(nwin, 10), ref.records())
+        np.testing.assert_array_equal(wsum.cpu().numpy(), ref.wsum)
+        assert tuple(br.shape) == (wl.B, wl.H, R)
+        if t not in check_attn:
+            continue
+        br_ref = {h: O.bridge_select(head(k, h)[0, 0], R, wl.Gh, wl.Gw) for h in heads}
+        b = br.cpu().numpy()
+        for h in heads:
+            np.testing.assert_array_equal(b[0, h], br_ref[h], err_msg=f"{wl.name} step {t} bridge head {h}")
+        out = A.area_window_attn(p, s, plan, wsum, br, q, k, v)
+        torch.cuda.synchronize()
+        rows = rows_for(wl, ref, seed=70 + t)
+        for h in heads:
+            o_ref = O.window_attention(head(q, h), head(k, h), head(v, h), ref, br_ref[h][None, None],
+                                       wl.Gh, wl.Gw, wl.rope_theta, rows=rows)
+            close(head(out, h)[:, :, rows], o_ref,
+                  f"{wl.name} pages' knobs step {t} (w={w}, R={R}, {nwin} windows) head {h}")

@@ -216,3 +216,33 @@ def test_step_rejects_bad_arguments_before_launch():
     assert L.area_attn_step(ctypes.byref(p), 0, 0, fake, fake, fake, fake, fake, fake, big, None) == -1
     assert L.area_attn_step(ctypes.byref(p), 0, 0, None, fake, fake, fake, fake, None, big, None) == -4
     assert L.area_attn_step(ctypes.byref(p), 9, 16, fake, fake, fake, fake, fake, fake, 64, None) == -4
+
+
+@pytest.mark.parametrize("name", ["tiny-32", "flux-2048", "flux-4096", "flux-6144", "qwen-6144x2048"])
+def test_schedule_at_pages_knobs_matches_oracle(name):
+    wl = W.get(name)
+    p = prob(name, **W.PAGES_KNOBS)
+    w0 = O.w_start_auto(wl.Gh, wl.Gw, wl.w_min)
+    sizes = O.window_sizes(w0, wl.w_min, wl.p2_steps)
+    for t, w in enumerate(sizes):
+        st = A.area_step_info(p, wl.p1_steps + t)
+        assert st["w"] == w, (name, t)
+        assert st["R"] == O.bridge_size(w, 1, 2), (name, t)
+    # configured knobs: fixed bridge at every window step, none on coarse steps
+    q = prob(name)
+    assert all(A.area_step_info(q, wl.p1_steps + t)["R"] == wl.bridge_k for t in range(wl.p2_steps))
+    assert A.area_step_info(q, 0)["R"] == 0
+
+
+def test_pages_knob_validation():
+    ok = prob("flux-2048", **W.PAGES_KNOBS)
+    A.area_validate(ok)
+    for over, status in [(dict(bridge_rho_num=1, bridge_rho_den=0), -1), (dict(halo_max=-1), -1),
+                         (dict(bridge_rho_num=-1), -1), (dict(w_start=63), -2)]:
+        with pytest.raises(A.AreaError) as e:
+            A.area_validate(prob("flux-2048", **over))
+        assert e.value.status == status, over
+    # a bridge whose cell grid cannot fit the image is rejected before anything runs
+    with pytest.raises(A.AreaError) as e:
+        A.area_validate(prob("tiny-32", bridge_rho_num=4, bridge_rho_den=1))
+    assert e.value.status == -2

@@ -90,6 +90,12 @@ WORKLOADS = {
 }
 
 
+# The pages' own Phase II knob values, as problem overrides: the first window
+# from the cost rule (w_start 0), Halo widths drawn per window up to 8, and a
+# bridge of (w/2)^2 tokens at window side w.
+PAGES_KNOBS = dict(w_start=0, halo_max=8, bridge_rho_num=1, bridge_rho_den=2)
+
+
 def get(name: str) -> Workload:
     return WORKLOADS[name]
 
