@@ -24,7 +24,14 @@ Sources (page titles, sections):
             repository layout.
 
 Where the pages leave a step open, the reading taken is marked READING and
-named (R1...R19); each is one small function here.
+named (R1...R20); each is one small function here.
+
+Text tokens (READING R20, [summary] Phase I: text tokens are never pooled,
+so each of the N image queries attends to T + N/f^2 keys): with T > 0 the
+token sequence is T text tokens first, then the Gh*Gw image tokens in
+row-major order.  Text tokens sit at RoPE position (0, 0) (no rotation),
+join every key set of both phases whole, and text queries attend densely to
+all T + N keys (text_attention).
 """
 from __future__ import annotations
 
@@ -78,6 +85,14 @@ def grid_positions(Gh: int, Gw: int) -> Tuple[np.ndarray, np.ndarray]:
     return n // Gw, n % Gw
 
 
+def token_positions(Gh: int, Gw: int, T: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Positions of the joint sequence: T text tokens at (0, 0) (READING R20),
+    then the image grid."""
+    y, x = grid_positions(Gh, Gw)
+    z = np.zeros(T, dtype=y.dtype)
+    return np.concatenate([z, y]), np.concatenate([z, x])
+
+
 # ----------------------------------------------------------------------------
 # Dense attention (the speedup baseline, and the inner step of both phases)
 # ----------------------------------------------------------------------------
@@ -102,17 +117,24 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def full_attention(q, k, v, Gh: int, Gw: int, theta: float,
-                   rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Uniform full attention over all N image tokens with RoPE at native
-    grid positions: the baseline AReA replaces ([summary] Overview and Main
+                   rows: Optional[np.ndarray] = None, T: int = 0) -> np.ndarray:
+    """Uniform full attention over all tokens with RoPE at native grid
+    positions: the baseline AReA replaces ([summary] Overview and Main
     Findings: speedups are quoted against full attention).  q, k, v are
-    un-rotated [B, H, N, D]; `rows` optionally restricts the output queries."""
-    y, x = grid_positions(Gh, Gw)
+    un-rotated [B, H, T + N, D]; `rows` optionally restricts the output
+    queries (indices into the joint sequence)."""
+    y, x = token_positions(Gh, Gw, T)
     kr = apply_rope_2d(k, y, x, theta)
     if rows is None:
-        rows = np.arange(Gh * Gw)
+        rows = np.arange(T + Gh * Gw)
     qr = apply_rope_2d(np.asarray(q)[..., rows, :], y[rows], x[rows], theta)
     return attention(qr, kr, v)
+
+
+def text_attention(q, k, v, Gh: int, Gw: int, theta: float, T: int) -> np.ndarray:
+    """READING R20: text queries take the dense path in every phase, over
+    all T + N keys at native positions; [B, H, T, D]."""
+    return full_attention(q, k, v, Gh, Gw, theta, rows=np.arange(T), T=T)
 
 
 # ----------------------------------------------------------------------------
@@ -144,27 +166,34 @@ def pool_tokens(t: np.ndarray, Gh: int, Gw: int, f: int, mode: int) -> np.ndarra
     return p.reshape(lead + ((Gh // f) * (Gw // f), D))
 
 
-def pool_kv(k, v, Gh: int, Gw: int, f: int, mode: int, theta: float):
+def pool_kv(k, v, Gh: int, Gw: int, f: int, mode: int, theta: float, T: int = 0):
     """Pooled keys (rotated at integer coarse positions (by, bx)) and pooled
     values (never rotated).  Keys are pooled before rotation so that the
     pooled key carries the coarse-grid position ([summary] Phase I: pooled
-    keys sit on the (W/f) x (H/f) grid)."""
-    kp = pool_tokens(k, Gh, Gw, f, mode)
-    vp = pool_tokens(v, Gh, Gw, f, mode)
+    keys sit on the (W/f) x (H/f) grid).  With T text tokens, the T text keys
+    (position (0, 0): unrotated) and values come first, unpooled ([summary]
+    Phase I: text tokens are never pooled)."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    kp = pool_tokens(k[..., T:, :], Gh, Gw, f, mode)
+    vp = pool_tokens(v[..., T:, :], Gh, Gw, f, mode)
     by, bx = grid_positions(Gh // f, Gw // f)
-    return apply_rope_2d(kp, by, bx, theta), vp
+    kp = apply_rope_2d(kp, by, bx, theta)
+    return np.concatenate([k[..., :T, :], kp], axis=-2), np.concatenate([v[..., :T, :], vp], axis=-2)
 
 
 def coarse_attention(q, kp_rot, vp, Gh: int, Gw: int, f: int, theta: float,
-                     rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Every full-resolution query attends to all pooled keys; its RoPE
-    position is its grid coordinate divided by f so that queries and pooled
-    keys share one coordinate system ([summary] Phase I).  Cost is N*N/f^2
-    query-key pairs, 1/f^2 of full attention."""
+                     rows: Optional[np.ndarray] = None, T: int = 0) -> np.ndarray:
+    """Every full-resolution image query attends to all pooled keys (and the
+    T text keys that pool_kv put first); its RoPE position is its grid
+    coordinate divided by f so that queries and pooled keys share one
+    coordinate system ([summary] Phase I).  Cost is N (T + N/f^2) query-key
+    pairs.  `rows` are image-token indices; image token n is row T + n of q."""
     y, x = grid_positions(Gh, Gw)
     if rows is None:
         rows = np.arange(Gh * Gw)
-    qr = apply_rope_2d(np.asarray(q)[..., rows, :], y[rows] / f, x[rows] / f, theta)
+    rows = np.asarray(rows)
+    qr = apply_rope_2d(np.asarray(q)[..., T + rows, :], y[rows] / f, x[rows] / f, theta)
     return attention(qr, kp_rot, vp)
 
 
@@ -592,16 +621,20 @@ def window_query_indices(win: Window, Gw: int) -> np.ndarray:
 
 
 def window_attention(q, k, v, plan: Plan, bridge: Optional[np.ndarray], Gh: int, Gw: int,
-                     theta: float, rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Phase II output [B, H, len(rows), D] (float64).
+                     theta: float, rows: Optional[np.ndarray] = None, T: int = 0) -> np.ndarray:
+    """Phase II output [B, H, len(rows), D] (float64) for image tokens `rows`.
 
     Each window's queries attend to the window's keys (Halo rectangle plus
-    outside bridge tokens) with RoPE at native grid positions; the outputs of
-    the windows covering a token are averaged with the windows' tent weights
-    (READING R15 of the centre-weighted blend, [summary] Phase II)."""
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    outside bridge tokens, plus the T text keys, READING R20) with RoPE at
+    native grid positions; the outputs of the windows covering a token are
+    averaged with the windows' tent weights (READING R15 of the
+    centre-weighted blend, [summary] Phase II).  q, k, v are [B, H, T + N, D]
+    with image token n at row T + n; bridge holds image-token indices."""
+    q = np.asarray(q, np.float64)[..., T:, :]
+    kt = np.asarray(k, np.float64)[..., :T, :]
+    vt = np.asarray(v, np.float64)[..., :T, :]
+    k = np.asarray(k, np.float64)[..., T:, :]
+    v = np.asarray(v, np.float64)[..., T:, :]
     B, H, N, D = q.shape
     y, x = grid_positions(Gh, Gw)
     kr = apply_rope_2d(k, y, x, theta)
@@ -622,7 +655,8 @@ def window_attention(q, k, v, plan: Plan, bridge: Optional[np.ndarray], Gh: int,
         for b in range(B):
             for h in range(H):
                 ki = window_key_indices(win, Gw, None if bridge is None else bridge[b, h])
-                o = attention(qr[b, h], kr[b, h, ki], v[b, h, ki])
+                o = attention(qr[b, h], np.concatenate([kt[b, h], kr[b, h, ki]]),
+                              np.concatenate([vt[b, h], v[b, h, ki]]))
                 acc[b, h, pos_of[qi]] += wt[:, None] * o
     ws = plan.wsum[rows].astype(np.float64)
     if np.any(ws <= 0):

@@ -605,3 +605,96 @@ def test_canvas_rules_from_pages():
 
 def test_step_phases_counts():
     assert O.step_phases(8, 20) == [1] * 8 + [2] * 20
+
+
+# ------------------------------------------------------------ text tokens ----
+# READING R20: T text tokens first, at RoPE position (0, 0), never pooled or windowed,
+# keys of every key set; text queries attend densely to all T + N keys.
+
+def _text_inputs(T, Gh, Gw, D=16, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [rng.standard_normal((1, 2, T + Gh * Gw, D)) for _ in range(3)]
+
+
+def test_text_phase1_key_count_from_pages():
+    # [summary] Phase I: text tokens are never pooled, so each of the N queries attends to T + N/f^2 keys
+    T, Gh, Gw, f = 5, 8, 12, 2
+    q, k, v = _text_inputs(T, Gh, Gw)
+    kp, vp = O.pool_kv(k, v, Gh, Gw, f, O.POOL_MEAN, 10000.0, T=T)
+    assert kp.shape[-2] == vp.shape[-2] == T + Gh * Gw // f ** 2
+    np.testing.assert_array_equal(kp[..., :T, :], k[..., :T, :])     # text keys unrotated, unpooled
+    np.testing.assert_array_equal(vp[..., :T, :], v[..., :T, :])
+
+
+def test_text_zero_queries_average_their_key_sets():
+    # q = 0 makes every score equal, so each output is the plain mean of its key set's values
+    T, Gh, Gw, f = 4, 8, 8, 2
+    _, k, v = _text_inputs(T, Gh, Gw, seed=1)
+    q = np.zeros_like(k)
+    full = O.full_attention(q, k, v, Gh, Gw, 10000.0, T=T)
+    np.testing.assert_allclose(full, np.broadcast_to(v.mean(axis=-2, keepdims=True), full.shape), atol=1e-12)
+    np.testing.assert_allclose(O.text_attention(q, k, v, Gh, Gw, 10000.0, T), full[..., :T, :], atol=1e-12)
+    kp, vp = O.pool_kv(k, v, Gh, Gw, f, O.POOL_MEAN, 10000.0, T=T)
+    co = O.coarse_attention(q, kp, vp, Gh, Gw, f, 10000.0, T=T)
+    np.testing.assert_allclose(co, np.broadcast_to(vp.mean(axis=-2, keepdims=True), co.shape), atol=1e-12)
+    plan = O.window_plan(Gh, Gw, 4, 1, 0, 0, None)
+    wo = O.window_attention(q, k, v, plan, None, Gh, Gw, 10000.0, T=T)
+    acc = np.zeros_like(wo)
+    for win in plan.windows:
+        ki = O.window_key_indices(win, Gw, None)
+        m = np.concatenate([v[..., :T, :], v[..., T + ki, :]], axis=-2).mean(axis=-2)
+        wt = np.outer(O.tent(win.qh), O.tent(win.qw)).reshape(-1)
+        for j, n in enumerate(O.window_query_indices(win, Gw)):
+            acc[..., n, :] += wt[j] * m
+    np.testing.assert_allclose(wo, acc / plan.wsum[None, None, :, None], atol=1e-12)
+
+
+def test_text_brute_force_tiny():
+    # direct double loops over explicit key lists, rotating each token at its own position
+    T, Gh, Gw, f, D, th = 3, 4, 6, 2, 8, 100.0
+    q, k, v = _text_inputs(T, Gh, Gw, D=D, seed=2)
+    ys, xs = O.token_positions(Gh, Gw, T)
+
+    def rot(t, y, x):
+        return O.apply_rope_2d(t[None, None, None, :], np.array([y]), np.array([x]), th)[0, 0, 0]
+
+    def softmax_out(qv, keys, vals):
+        s = np.array([qv @ kk for kk in keys]) / math.sqrt(D)
+        e = np.exp(s - s.max())
+        return (e[:, None] * np.array(vals)).sum(0) / e.sum()
+
+    b, h = 0, 1
+    kr = [rot(k[b, h, i], ys[i], xs[i]) for i in range(T + Gh * Gw)]
+    # full attention and text queries
+    full = O.full_attention(q, k, v, Gh, Gw, th, T=T)
+    for i in (0, T - 1, T, T + 7, T + Gh * Gw - 1):
+        want = softmax_out(rot(q[b, h, i], ys[i], xs[i]), kr, list(v[b, h]))
+        np.testing.assert_allclose(full[b, h, i], want, rtol=1e-10, atol=1e-12)
+    # coarse: image query n at (y/f, x/f) against text keys + block-mean keys at block positions
+    kp, vp = O.pool_kv(k, v, Gh, Gw, f, O.POOL_MEAN, th, T=T)
+    co = O.coarse_attention(q, kp, vp, Gh, Gw, f, th, T=T)
+    keys = [k[b, h, i] for i in range(T)]
+    vals = [v[b, h, i] for i in range(T)]
+    for by in range(Gh // f):
+        for bx in range(Gw // f):
+            blk = [T + (by * f + a) * Gw + bx * f + c for a in range(f) for c in range(f)]
+            keys.append(rot(np.mean([k[b, h, i] for i in blk], axis=0), by, bx))
+            vals.append(np.mean([v[b, h, i] for i in blk], axis=0))
+    for n in (0, 5, Gh * Gw - 1):
+        y, x = divmod(n, Gw)
+        want = softmax_out(rot(q[b, h, T + n], y / f, x / f), keys, vals)
+        np.testing.assert_allclose(co[b, h, n], want, rtol=1e-10, atol=1e-12)
+    # window: text keys + the window's Halo rectangle
+    plan = O.window_plan(Gh, Gw, 4, 1, 0, 0, None)
+    wo = O.window_attention(q, k, v, plan, None, Gh, Gw, th, T=T)
+    for n in (0, 9, Gh * Gw - 1):
+        y, x = divmod(n, Gw)
+        acc, wsum = 0.0, 0
+        for win in plan.windows:
+            if not (win.qy0 <= y < win.qy0 + win.qh and win.qx0 <= x < win.qx0 + win.qw):
+                continue
+            ki = list(range(T)) + [T + i for i in O.window_key_indices(win, Gw, None)]
+            o = softmax_out(rot(q[b, h, T + n], y, x), [kr[i] for i in ki], [v[b, h, i] for i in ki])
+            w = min(y - win.qy0 + 1, win.qh - (y - win.qy0)) * min(x - win.qx0 + 1, win.qw - (x - win.qx0))
+            acc, wsum = acc + w * o, wsum + w
+        np.testing.assert_allclose(wo[b, h, n], acc / wsum, rtol=1e-10, atol=1e-12)
