@@ -21,8 +21,8 @@
  * Conventions shared by every call
  * --------------------------------
  *  * Tensors are caller-owned, contiguous DEVICE buffers.  Q, K, V and the
- *    outputs are bfloat16 laid out [B][H][Gh*Gw][D]; image token n sits at
- *    grid row y = n / Gw, column x = n % Gw.  Q and K are passed WITHOUT
+ *    outputs are bfloat16 laid out [B][H][T+Gh*Gw][D] (token sequences,
+ *    below); image token n sits at grid row y = n / Gw, column x = n % Gw.  Q and K are passed WITHOUT
  *    rotary embedding: the library rotates them itself (two-axis RoPE: the
  *    first D/2 channels encode y, the last D/2 encode x, channel pair
  *    (2k, 2k+1) of an axis half turns by pos * theta^(-4k/D)).
@@ -93,12 +93,23 @@ extern "C" {
 #define AREA_PH_QTOT  10       /* sum of query-rect areas over all windows      */
 /* record fields: qy0 qx0 qh qw  ky0 kx0 kh kw  parent quadrant(-1 | 0..3) */
 
+/* ---- token sequences ----------------------------------------------------
+ * Every q, k, v and out tensor is [B][H][T + Gh*Gw][D]: T text tokens first,
+ * then the image tokens in row-major order (image token (y, x) is row
+ * T + y*Gw + x).  Text tokens sit at RoPE position (0, 0), i.e. are not
+ * rotated; they are never pooled (ai.info summary, Methodology, Phase I:
+ * each of the N image queries attends to T + N/f^2 keys) and join every
+ * Phase II key set whole.  The image-query calls (area_coarse_attn,
+ * area_window_attn) write the image rows of out; text queries take the dense
+ * path over all T + N keys (area_text_attn).  area_full_attn writes every
+ * row.  T = 0 gives the image-only layout [B][H][Gh*Gw][D]. */
+
 /* ---- problem description ------------------------------------------------ */
 typedef struct area_problem {
   int32_t B, H, D;            /* batch, heads, head dim (64 or 128)              */
   int32_t Gh, Gw;             /* image token grid (rows, columns)                */
   int32_t native_h, native_w; /* the model's native token grid                   */
-  int32_t T;                  /* text tokens joined to every key set (must be 0) */
+  int32_t T;                  /* text tokens ahead of the image tokens (0 = none) */
   float   rope_theta;         /* RoPE base, e.g. 10000                           */
   int32_t p1_steps;           /* Phase I (coarse) steps                          */
   int32_t f0;                 /* first pooling factor; 0 = derive from native    */
@@ -184,8 +195,8 @@ const char* area_last_error(void);
 /* ---- device calls ------------------------------------------------------- */
 
 /* Phase I pooling (blog Fase I; ai.info summary Phase I; README Phase I
- * bullet).  k, v: [B][H][Gh*Gw][D] bf16, un-rotated.  kp, vp: outputs
- * [B][H][(Gh/f)*(Gw/f)][D] in IEEE fp16 (the attention operand type, three
+ * bullet).  k, v: [B][H][T+Gh*Gw][D] bf16, un-rotated.  kp, vp: outputs
+ * [B][H][T+(Gh/f)*(Gw/f)][D] in IEEE fp16 (the attention operand type, three
  * mantissa bits finer than bf16).  Block (by, bx) sits at index
  * by*(Gw/f)+bx.
  * kp = RoPE(pool(k)) at integer coarse position (by, bx); vp = pool(v).
@@ -196,8 +207,9 @@ int area_pool_kv(const area_problem* p, int f, const void* k, const void* v,
 
 /* Phase I cross-scale coarse attention (ai.info summary, Methodology,
  * Phase I): out = softmax(RoPE(q at (y/f, x/f)) kp^T / sqrt(D)) vp for every
- * full-resolution query.  q: [B][H][Gh*Gw][D] bf16 un-rotated; kp, vp as
- * produced by area_pool_kv; out: [B][H][Gh*Gw][D] bf16.  Workspace:
+ * full-resolution image query (and the T text keys that area_pool_kv puts
+ * first).  q: [B][H][T+Gh*Gw][D] bf16 un-rotated; kp, vp as produced by
+ * area_pool_kv; out: [B][H][T+Gh*Gw][D] bf16, image rows written.  Workspace:
  * area_workspace_bytes(p, AREA_OP_COARSE). kp and vp are fp16 as produced by
  * area_pool_kv. */
 int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp,
@@ -216,7 +228,8 @@ int area_dwt_detail(const area_problem* p, int C, const float* latent, float* en
  * Phase II; README repository layout: tiling = base tiling, DWT map,
  * splits, Halo, merge weights; bridge = bridge token selection).
  *  energy_q: [Gh/2][Gw/2] int32 from area_dwt_detail (NULL: no splits).
- *  k: [B][H][Gh*Gw][D] bf16 un-rotated keys, used for the bridge (NULL or
+ *  k: [B][H][T+Gh*Gw][D] bf16 un-rotated keys; the bridge is chosen among
+ *     the image tokens (NULL or
  *     p->bridge_k == 0: no bridge).
  * Outputs (device):
  *  plan:   area_plan_words(p) int32: header + window records in canonical
@@ -248,7 +261,8 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
  * native positions, softmax(q k^T / sqrt(D)) v; each token's output is the
  * tent-weighted average of the outputs of the windows covering it (divided
  * by wsum).  `step` must be the step the plan was built for.  q, k, v:
- * [B][H][Gh*Gw][D] bf16 un-rotated; out: same layout.  bridge_idx may be
+ * [B][H][T+Gh*Gw][D] bf16 un-rotated; out: same layout, image rows written
+ * (each window's key set also holds the T text keys).  bridge_idx may be
  * NULL when the plan has R == 0.  Workspace:
  * area_workspace_bytes(p, AREA_OP_WINDOW). */
 int area_window_attn(const area_problem* p, int step, const int32_t* plan, const int32_t* wsum,
@@ -262,6 +276,15 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v,
                    void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Text queries of a joint sequence (p->T > 0): the T text rows of out get
+ * dense attention over all T + Gh*Gw keys with RoPE at native positions
+ * (text at (0, 0)) -- the path text queries take in every phase, since only
+ * the image keys are pooled or windowed.  Layouts as area_full_attn; only
+ * rows 0 .. T-1 of out are written.  Does nothing when p->T == 0.
+ * Workspace: area_workspace_bytes(p, AREA_OP_FULL). */
+int area_text_attn(const area_problem* p, const void* q, const void* k, const void* v,
+                   void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* One attention call of denoising step `step` along the schedule: the
  * pages run Phase I (pooled coarse attention over the pooling ramp) for the
  * first p1_steps denoising steps and Phase II (windowed attention) after
@@ -270,12 +293,12 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
  * setup note on native resolution).  Dispatches by area_step_info():
  *  AREA_PHASE_FULL:   area_full_attn;
  *  AREA_PHASE_COARSE: area_pool_kv with the step's factor f, then
- *                     area_coarse_attn;
+ *                     area_coarse_attn (and area_text_attn when T > 0);
  *  AREA_PHASE_WINDOW: area_dwt_detail of `latent` (C channels, [C][Gh][Gw]
  *                     fp32; NULL: no quadrant splits), area_window_plan
- *                     (with the bridge when p->bridge_k > 0) and
- *                     area_window_attn.
- * q, k, v: [B][H][Gh*Gw][D] bf16 un-rotated; out: same layout.  Every
+ *                     (with the bridge when the step has one),
+ *                     area_window_attn (and area_text_attn when T > 0).
+ * q, k, v: [B][H][T+Gh*Gw][D] bf16 un-rotated; out: same layout.  Every
  * intermediate (pooled K/V, energy map, plan, weight sums, bridge indices)
  * lives in the caller's workspace of area_workspace_bytes(p, AREA_OP_STEP)
  * bytes; nothing is allocated.  Results are identical to calling the

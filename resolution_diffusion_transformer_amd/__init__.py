@@ -18,7 +18,8 @@ __all__ = [
     "AreaError", "Problem", "lib", "library_path", "exported_symbols",
     "area_validate", "area_step_info", "area_f0", "area_base_windows", "area_workspace_bytes",
     "area_plan_words", "area_pool_kv", "area_coarse_attn", "area_dwt_detail",
-    "area_window_plan", "area_window_attn", "area_full_attn", "area_attn_step", "area_set_attn_events",
+    "area_window_plan", "area_window_attn", "area_full_attn", "area_text_attn", "area_attn_step",
+    "area_set_attn_events",
     "POOL_MEAN", "POOL_CENTER", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
     "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "OP_STEP", "PLAN_HEADER", "PLAN_REC",
 ]
@@ -101,6 +102,11 @@ class Problem:
     def N(self) -> int:
         return self.Gh * self.Gw
 
+    @property
+    def L(self) -> int:
+        """Rows per sequence: T text tokens, then the image tokens."""
+        return self.T + self.Gh * self.Gw
+
 
 _LIB = None
 
@@ -123,6 +129,8 @@ _SIGS = {
     "area_window_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 8
                          + [ctypes.c_size_t, ctypes.c_void_p]),
     "area_full_attn": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5
+                       + [ctypes.c_size_t, ctypes.c_void_p]),
+    "area_text_attn": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5
                        + [ctypes.c_size_t, ctypes.c_void_p]),
     "area_attn_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 6
                        + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -246,10 +254,10 @@ def workspace(p: Problem, op: int, device="cuda"):
 
 def area_pool_kv(p: Problem, f: int, k, v, kp=None, vp=None):
     torch = _torch()
-    shp = (p.B, p.H, p.N, p.D)
+    shp = (p.B, p.H, p.L, p.D)
     _need(k, torch.bfloat16, shp, "k")
     _need(v, torch.bfloat16, shp, "v")
-    M = (p.Gh // f) * (p.Gw // f) if f > 0 else 0
+    M = p.T + ((p.Gh // f) * (p.Gw // f) if f > 0 else 0)
     kp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float16, device=k.device) if kp is None else kp
     vp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float16, device=k.device) if vp is None else vp
     _need(kp, torch.float16, (p.B, p.H, M, p.D), "kp")
@@ -261,12 +269,12 @@ def area_pool_kv(p: Problem, f: int, k, v, kp=None, vp=None):
 
 def area_coarse_attn(p: Problem, f: int, q, kp, vp, out=None, ws=None):
     torch = _torch()
-    _need(q, torch.bfloat16, (p.B, p.H, p.N, p.D), "q")
-    M = (p.Gh // f) * (p.Gw // f) if f > 0 else 0
+    _need(q, torch.bfloat16, (p.B, p.H, p.L, p.D), "q")
+    M = p.T + ((p.Gh // f) * (p.Gw // f) if f > 0 else 0)
     _need(kp, torch.float16, (p.B, p.H, M, p.D), "kp")
     _need(vp, torch.float16, (p.B, p.H, M, p.D), "vp")
     out = torch.empty_like(q) if out is None else out
-    _need(out, torch.bfloat16, (p.B, p.H, p.N, p.D), "out")
+    _need(out, torch.bfloat16, (p.B, p.H, p.L, p.D), "out")
     ws = workspace(p, OP_COARSE, q.device) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_coarse_attn(ref, f, _ptr(q), _ptr(kp), _ptr(vp), _ptr(out), _ptr(ws),
@@ -295,7 +303,7 @@ def area_window_plan(p: Problem, step: int, energy_q, k, plan=None, wsum=None, b
     if energy_q is not None:
         _need(energy_q, torch.int32, (p.Gh // 2, p.Gw // 2), "energy_q")
     if k is not None:
-        _need(k, torch.bfloat16, (p.B, p.H, p.N, p.D), "k")
+        _need(k, torch.bfloat16, (p.B, p.H, p.L, p.D), "k")
     words = area_plan_words(p)
     plan = torch.zeros(words, dtype=torch.int32, device=dev) if plan is None else plan
     wsum = torch.empty(p.N, dtype=torch.int32, device=dev) if wsum is None else wsum
@@ -317,7 +325,7 @@ def area_window_plan(p: Problem, step: int, energy_q, k, plan=None, wsum=None, b
 
 def area_window_attn(p: Problem, step: int, plan, wsum, bridge_idx, q, k, v, out=None, ws=None):
     torch = _torch()
-    shp = (p.B, p.H, p.N, p.D)
+    shp = (p.B, p.H, p.L, p.D)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, shp, nm)
     _need(plan, torch.int32, (area_plan_words(p),), "plan")
@@ -334,12 +342,27 @@ def area_window_attn(p: Problem, step: int, plan, wsum, bridge_idx, q, k, v, out
     return out
 
 
+def area_text_attn(p: Problem, q, k, v, out=None, ws=None):
+    """Text-query rows (0 .. T-1) of out: dense attention over all T + N keys."""
+    torch = _torch()
+    shp = (p.B, p.H, p.L, p.D)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, shp, nm)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, torch.bfloat16, shp, "out")
+    ws = workspace(p, OP_FULL, q.device) if ws is None else ws
+    s, ref = _pp(p)
+    _check(lib().area_text_attn(ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
 def area_attn_step(p: Problem, step: int, latent, q, k, v, out=None, ws=None):
     """One denoising step's attention along the schedule (full, pooled
     coarse, or windowed with plan and bridge); latent [C, Gh, Gw] fp32 feeds
     the detail map of window steps (None: no quadrant splits)."""
     torch = _torch()
-    shp = (p.B, p.H, p.N, p.D)
+    shp = (p.B, p.H, p.L, p.D)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, shp, nm)
     C = 0
@@ -357,7 +380,7 @@ def area_attn_step(p: Problem, step: int, latent, q, k, v, out=None, ws=None):
 
 def area_full_attn(p: Problem, q, k, v, out=None, ws=None):
     torch = _torch()
-    shp = (p.B, p.H, p.N, p.D)
+    shp = (p.B, p.H, p.L, p.D)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.bfloat16, shp, nm)
     out = torch.empty_like(q) if out is None else out
@@ -374,6 +397,6 @@ def problem_for(wl, **over) -> Problem:
     kw = dict(B=wl.B, H=wl.H, D=wl.D, Gh=wl.Gh, Gw=wl.Gw, native_h=wl.native_h,
               native_w=wl.native_w, rope_theta=wl.rope_theta, p1_steps=wl.p1_steps, f0=0,
               f_min=wl.f_min, pool_mode=POOL_MEAN, p2_steps=wl.p2_steps, w_start=wl.w_start,
-              w_min=wl.w_min, halo=wl.halo, bridge_k=wl.bridge_k, seed=wl.seed)
+              w_min=wl.w_min, halo=wl.halo, bridge_k=wl.bridge_k, seed=wl.seed, T=getattr(wl, "T", 0))
     kw.update(over)
     return Problem(**kw)

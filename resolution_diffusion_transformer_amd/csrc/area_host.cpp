@@ -216,8 +216,8 @@ int window_step(const area_problem& p, int step, WindowStepInfo& out) {
   int64_t hw = p.halo_max > 0 ? p.halo_max : p.halo;
   int64_t kh = std::min<int64_t>(Ly + 2 * hw, p.Gh), kw = std::min<int64_t>(Lx + 2 * hw, p.Gw);
   int64_t qh = std::min<int64_t>(Ly - h1 + 2 * hw, p.Gh), qw = std::min<int64_t>(Lx - w1 + 2 * hw, p.Gw);
-  int64_t g_unsplit = ceil_div(kh * kw + R, kAttnBN);
-  int64_t g_split = 4 * ceil_div(qh * qw + R, kAttnBN);
+  int64_t g_unsplit = ceil_div(kh * kw + R + p.T, kAttnBN);
+  int64_t g_split = 4 * ceil_div(qh * qw + R + p.T, kAttnBN);
   out.max_gtiles = nb * (g_unsplit > g_split ? g_unsplit : g_split);
   return AREA_OK;
 }
@@ -230,7 +230,7 @@ static int validate(const area_problem* pp) {
   if (p.B < 1 || p.H < 1 || p.Gh < 1 || p.Gw < 1 || p.native_h < 1 || p.native_w < 1)
     return fail(AREA_E_INVALID, "B, H, Gh, Gw, native_h, native_w must be positive");
   if (p.D != 64 && p.D != 128) return fail(AREA_E_UNSUPPORTED, pstr("head dim D must be 64 or 128, D", p.D));
-  if (p.T != 0) return fail(AREA_E_UNSUPPORTED, pstr("text tokens are not supported yet, T", p.T));
+  if (p.T < 0 || p.T > (1 << 20)) return fail(AREA_E_INVALID, pstr("text tokens must be in 0 .. 2^20, T", p.T));
   if (!(p.rope_theta > 0.0f) || !std::isfinite(p.rope_theta))
     return fail(AREA_E_INVALID, "rope_theta must be positive and finite");
   if (p.p1_steps < 0 || p.p2_steps < 0) return fail(AREA_E_INVALID, "step counts must be >= 0");
@@ -243,7 +243,7 @@ static int validate(const area_problem* pp) {
     return fail(AREA_E_INVALID, "bridge_rho_num >= 0, and bridge_rho_den > 0 when it is used");
   if (p.split_den <= 0 || p.split_num < 0) return fail(AREA_E_INVALID, "split_num >= 0, split_den > 0");
   long long N = (long long)p.Gh * p.Gw;
-  if (N > (1LL << 30) || (long long)p.B * p.H * N * p.D > (1LL << 40))
+  if (N + p.T > (1LL << 30) || (long long)p.B * p.H * (N + p.T) * p.D > (1LL << 40))
     return fail(AREA_E_UNSUPPORTED, "problem too large");
   if (p.Gh % 2 || p.Gw % 2) return fail(AREA_E_SHAPE, "both grid sides must be even");
   if (canvas_gated(p)) return AREA_OK;  // full attention only; the knobs below are unused
@@ -273,7 +273,8 @@ static int validate(const area_problem* pp) {
 
 static int64_t BH_of(const area_problem& p) { return (int64_t)p.B * p.H; }
 static int64_t N_of(const area_problem& p) { return (int64_t)p.Gh * p.Gw; }
-static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * N_of(p) * p.D * 2; }
+static int64_t L_of(const area_problem& p) { return (int64_t)p.T + N_of(p); }  // rows per sequence
+static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * L_of(p) * p.D * 2; }
 
 struct WindowMax {
   int64_t q_total = 0, max_items = 0, max_gtiles = 0;
@@ -350,11 +351,12 @@ static StepLayout step_layout(const area_problem& p) {
       int f = ramp_factor(p, f0, s);
       M = std::max(M, N / ((size_t)f * f));
     }
-    const size_t pooled = align_up(BH * M * p.D * 2);
+    const size_t pooled = align_up(BH * (M + p.T) * p.D * 2);
     l.kp = 0;
     l.vp = pooled;
     l.coarse_ws = 2 * pooled;
-    coarse = l.coarse_ws + workspace_bytes(p, AREA_OP_COARSE);
+    coarse = l.coarse_ws + std::max(workspace_bytes(p, AREA_OP_COARSE),
+                                     p.T > 0 ? workspace_bytes(p, AREA_OP_FULL) : (size_t)0);
   }
   if (p.p2_steps > 0) {
     size_t o = 0;
@@ -369,7 +371,8 @@ static StepLayout step_layout(const area_problem& p) {
     l.bridge = o;
     o += align_up(BH * std::max(window_max(p).max_R, 1) * 4);
     l.window_ws = o;
-    window = o + std::max(workspace_bytes(p, AREA_OP_PLAN), workspace_bytes(p, AREA_OP_WINDOW));
+    window = o + std::max({workspace_bytes(p, AREA_OP_PLAN), workspace_bytes(p, AREA_OP_WINDOW),
+                           p.T > 0 ? workspace_bytes(p, AREA_OP_FULL) : (size_t)0});
   }
   l.total = std::max(coarse, window);
   return l;
@@ -380,9 +383,9 @@ static size_t workspace_bytes(const area_problem& p, int op) {
     case AREA_OP_STEP:
       return step_layout(p).total;
     case AREA_OP_FULL:
-      return 2 * align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)N_of(p), p.D));
+      return 2 * align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D));
     case AREA_OP_COARSE:
-      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)N_of(p), p.D));
+      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D));
     case AREA_OP_PLAN: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
       WindowMax m = window_max(p);
@@ -515,7 +518,7 @@ int area_pool_kv(const area_problem* p, int f, const void* k, const void* v, voi
   if (rc) return rc;
   if (!k || !v || !kp || !vp) return fail(AREA_E_INVALID, "NULL tensor");
   if (f < 1 || p->Gh % f || p->Gw % f) return fail(AREA_E_SHAPE, pstr("f must divide both grid sides, f", f));
-  return launch_pool(k, v, kp, vp, BH_of(*p), p->Gh, p->Gw, p->D, f, p->pool_mode, p->rope_theta, stream);
+  return launch_pool(k, v, kp, vp, BH_of(*p), p->T, p->Gh, p->Gw, p->D, f, p->pool_mode, p->rope_theta, stream);
 }
 
 int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp, const void* vp,
@@ -531,12 +534,12 @@ int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp
   int M = N / (f * f);
   char* qr = (char*)ws;
   char* vt = qr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, nullptr, nullptr, qr, nullptr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
+  rc = launch_prep(q, nullptr, nullptr, qr, nullptr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
                    stream);
   if (rc) return rc;
-  rc = launch_vt(vp, vt, BH, M, p->D, false, stream);
+  rc = launch_vt(vp, vt, BH, p->T + M, p->D, false, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kp, vt, out, BH, N, M, p->D, stream);
+  return launch_dense_attn(qr, kp, vt, out, BH, N, p->T, p->T + N, p->T + M, p->D, stream);
 }
 
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out,
@@ -551,11 +554,32 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
   char* qr = (char*)ws;
   char* kr = qr + align_up(tok_bytes(*p));
   char* vt = kr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
   if (rc) return rc;
-  rc = launch_vt(v, vt, BH, N, p->D, true, stream);
+  const int L = p->T + N;
+  rc = launch_vt(v, vt, BH, L, p->D, true, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kr, vt, out, BH, N, N, p->D, stream);
+  return launch_dense_attn(qr, kr, vt, out, BH, L, 0, L, L, p->D, stream);
+}
+
+int area_text_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int rc = validate(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
+  if (p->T == 0) return AREA_OK;
+  rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
+  if (rc) return rc;
+  int64_t BH = BH_of(*p);
+  const int L = (int)L_of(*p);
+  char* qr = (char*)ws;
+  char* kr = qr + align_up(tok_bytes(*p));
+  char* vt = kr + align_up(tok_bytes(*p));
+  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  if (rc) return rc;
+  rc = launch_vt(v, vt, BH, L, p->D, true, stream);
+  if (rc) return rc;
+  return launch_dense_attn(qr, kr, vt, out, BH, p->T, 0, L, L, p->D, stream);
 }
 
 int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
@@ -607,7 +631,7 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
   if (use_bridge) {
     int rh, rw;
     bridge_cells(wi.R, p->Gh, p->Gw, rh, rw);
-    rc = launch_bridge(k, bridge_idx, BH_of(*p), p->Gh, p->Gw, p->D, wi.R, rh, rw,
+    rc = launch_bridge(k, bridge_idx, BH_of(*p), p->T, p->Gh, p->Gw, p->D, wi.R, rh, rw,
                        wsb + align_up(plan_ws_bytes(m.n_base)), stream);
   }
   return rc;
@@ -630,6 +654,7 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   a.Gw = p->Gw;
   a.D = p->D;
   a.R = (bridge_idx && wi.R > 0) ? wi.R : 0;
+  a.T = p->T;
   a.BH = BH_of(*p);
   a.max_windows = 4 * wi.ty.n * wi.tx.n;
   a.max_items = wi.max_items;
@@ -649,7 +674,7 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   w.vg = base + l.vg;
   w.blist = (int*)(base + l.blist);
   w.bcount = (int*)(base + l.bcount);
-  rc = launch_prep(q, k, nullptr, base + l.q, base + l.k, nullptr, a.BH, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
+  rc = launch_prep(q, k, nullptr, base + l.q, base + l.k, nullptr, a.BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
                    stream);
   if (rc) return rc;
   return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, base + l.q, base + l.k, v, out, w, stream);
@@ -674,7 +699,9 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       void* vp = base + l.vp;
       rc = area_pool_kv(p, st.f, k, v, kp, vp, stream);
       if (rc) return rc;
-      return area_coarse_attn(p, st.f, q, kp, vp, out, base + l.coarse_ws, ws_bytes - l.coarse_ws, stream);
+      rc = area_coarse_attn(p, st.f, q, kp, vp, out, base + l.coarse_ws, ws_bytes - l.coarse_ws, stream);
+      if (rc) return rc;
+      return area_text_attn(p, q, k, v, out, base + l.coarse_ws, ws_bytes - l.coarse_ws, stream);
     }
     default: {
       float* energy = (float*)(base + l.energy);
@@ -689,8 +716,10 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       rc = area_window_plan(p, step, latent ? energy_q : nullptr, k, plan, wsum, bridge, base + l.window_ws,
                             ws_bytes - l.window_ws, stream);
       if (rc) return rc;
-      return area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
-                              ws_bytes - l.window_ws, stream);
+      rc = area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
+                            ws_bytes - l.window_ws, stream);
+      if (rc) return rc;
+      return area_text_attn(p, q, k, v, out, base + l.window_ws, ws_bytes - l.window_ws, stream);
     }
   }
 }

@@ -82,9 +82,10 @@ typedef void* stream_t;
 
 // fp16 attention operands: qo = RoPE(q), ko = RoPE(k) at grid positions
 // (row / div, column / div), vo = v; k/ko and v/vo may be null.
+// Sequences are T text tokens (position (0, 0)) then the Gh x Gw image grid.
 int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
-                int Gh, int Gw, int D, float theta, float div, stream_t s);
-int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int Gh, int Gw,
+                int T, int Gh, int Gw, int D, float theta, float div, stream_t s);
+int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw,
                 int D, int f, int mode, float theta, stream_t s);
 int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int Gh, int Gw,
                stream_t s);
@@ -101,7 +102,7 @@ int launch_plan(const PlanArgs& a, const int32_t* energy_q, int32_t* plan, int32
                 void* ws, stream_t s);
 size_t plan_ws_bytes(int n_base);
 
-int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D, int R, int rh,
+int launch_bridge(const void* k, int32_t* idx, int64_t BH, int T, int Gh, int Gw, int D, int R, int rh,
                   int rw, void* ws, stream_t s);
 constexpr int kBridgeSortMax = 4096;  // cells per row of the bridge cell grid
 size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
@@ -113,11 +114,14 @@ int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, s
 
 // Attention over fp16 operands (rotated q, rotated k rows, V^T tiles), bf16
 // output.
+// Queries are rows q0 .. q0 + Nq - 1 of sequences of q_rows rows (q and out
+// share that layout); keys are the Nk rows of k_rot / vt per (batch, head).
 int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH,
-                      int Nq, int Nk, int D, stream_t s);
+                      int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
 
 struct WindowAttnArgs {
   int Gh, Gw, D, R;
+  int T;                          // text tokens ahead of the image rows, joined to every key set
   int64_t BH;
   int max_windows;
   int64_t max_items, max_gtiles;

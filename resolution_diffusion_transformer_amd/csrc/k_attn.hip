@@ -136,7 +136,8 @@ ItemsWs make_items_ws(void* ws, int max_windows, int n_base, int64_t max_items) 
 }
 
 // One block: slot offsets (prefix of query areas in record order), key-tile
-// offsets (prefix of ceil((kh kw + R) / 64)), the first record of every base
+// offsets (prefix of ceil((kh kw + R) / 64), R the bridge and text keys a
+// window can add), the first record of every base
 // window, the (record, query tile) list -- whole windows first, quadrants
 // after (largest key sets first) -- and the (record, key tile) list.
 __global__ __launch_bounds__(256) void items_kernel(const int32_t* __restrict__ plan, ItemsWs w, int BM, int R,
@@ -229,15 +230,16 @@ __global__ __launch_bounds__(256) void bridge_compact_kernel(const int32_t* __re
 
 // Gathers one 64-key tile of a window's key set: slot s < kh*kw is the Halo
 // rectangle token s (row-major), then the compacted outside bridge tokens,
-// then zero rows.  K rows are copied (already rotated, fp16); V rows are
-// converted bf16 -> fp16 and written transposed.
+// then the T text tokens, then zero rows.  Sequences hold the T text rows
+// first, image token n at row T + n.  K rows are copied (already rotated,
+// fp16); V rows are converted bf16 -> fp16 and written transposed.
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan, const int* __restrict__ gtiles,
                                                      const int* __restrict__ n_items, const int* __restrict__ kv_tile_off,
                                                      const int* __restrict__ list, const int* __restrict__ count,
                                                      const u16* __restrict__ kr, const u16* __restrict__ v,
                                                      u16* __restrict__ kg, u16* __restrict__ vg, int64_t cap_tiles,
-                                                     int R, int Gw, int N, int64_t BH) {
+                                                     int R, int Tt, int Gw, int N, int64_t BH) {
   constexpr int CPR = D / 8;
   constexpr int LS = D + 8;
   __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
@@ -253,18 +255,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   const int T = kv_tile_off[rec] + t;
   if (threadIdx.x < BN) {
     int s = t * BN + threadIdx.x;
-    int tok = -1;
+    int row = -1;  // sequence row of the slot's token
     if (s < nrect) {
       int yy = s / kw;
-      tok = (ky0 + yy) * Gw + kx0 + (s - yy * kw);
+      row = Tt + (ky0 + yy) * Gw + kx0 + (s - yy * kw);
     } else if (s - nrect < cnt) {
-      tok = list[((int64_t)rec * BH + bh) * R + (s - nrect)];
+      row = Tt + list[((int64_t)rec * BH + bh) * R + (s - nrect)];
+    } else if (s - nrect - cnt < Tt) {
+      row = s - nrect - cnt;
     }
-    s_tok[threadIdx.x] = tok;
+    s_tok[threadIdx.x] = row;
   }
   __syncthreads();
-  const u16* ksrc = kr + bh * (int64_t)N * D;
-  const u16* vsrc = v + bh * (int64_t)N * D;
+  const u16* ksrc = kr + bh * (int64_t)(Tt + N) * D;
+  const u16* vsrc = v + bh * (int64_t)(Tt + N) * D;
   u16* kdst = kg + (bh * cap_tiles + T) * (int64_t)BN * D;
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
     int row = c / CPR, col = c - row * CPR;
@@ -294,12 +298,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 
 // -------------------------------------------------------------- attention --
 struct AttnArgs {
-  const u16* q;        // rotated queries, fp16 [BH][Nq][D]
+  const u16* q;        // rotated queries, fp16 [BH][q_rows][D]
   const u16* k;        // fp16 key rows [BH][k_rows][D]
   const u16* vt;       // fp16 V^T tiles [BH][k_tiles][D][64]
-  u16* out;            // bf16 [BH][Nq][D]
+  u16* out;            // bf16 [BH][q_rows][D]
   int64_t BH;
-  int Nq;
+  int Nq;              // dense mode: queries per head, rows q0 .. q0 + Nq - 1
+  int q0, q_rows;      // first query row (window mode: image token n is row q0 + n); rows per head
   int64_t k_rows, k_tiles;  // per-(batch*head) strides of k and vt
   int n_kv;            // dense mode: keys per query
   int n_qtiles;        // dense mode: query tiles per head
@@ -314,7 +319,7 @@ struct AttnArgs {
   const int* kv_tile_off;  // per record: first gathered key tile
   const int* bcount;       // [record][BH] bridge tokens kept
   float* slots;            // [slot][BH][D] fp32 outputs of overlapped tokens
-  int Gw, R;
+  int Gw, R, T;         // T text keys end every window's key set
   int64_t max_items;
 };
 
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
     const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
     qy0 = rp[0]; qx0 = rp[1]; qh = rp[2]; qw = rp[3];
     nq = qh * qw;
-    nkv = rp[6] * rp[7] + (a.R > 0 ? a.bcount[(int64_t)rec * a.BH + bh] : 0);
+    nkv = rp[6] * rp[7] + (a.R > 0 ? a.bcount[(int64_t)rec * a.BH + bh] : 0) + a.T;
     t0 = a.kv_tile_off[rec];
   } else {
     bh = L / a.n_qtiles;
@@ -529,7 +534,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
   }
   const u16* kbase = a.k + bh * a.k_rows * D + t0 * BN * D;
   const u16* vtbase = a.vt + (bh * a.k_tiles + t0) * (int64_t)D * BN;
-  const u16* qbase = a.q + bh * (int64_t)a.Nq * D;
+  const u16* qbase = a.q + (bh * (int64_t)a.q_rows + a.q0) * D;
 
   // ---- queries of this lane
   int qtok[QG];
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
       direct = a.wsum[qtok[g]] == wt;
     }
     if (direct) {
-      u16* orow = a.out + (bh * (int64_t)a.Nq + qtok[g]) * D;
+      u16* orow = a.out + (bh * (int64_t)a.q_rows + a.q0 + qtok[g]) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -659,6 +664,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
 // ------------------------------------------------------------------ blend --
 struct BlendArgs {
   int Gh, Gw, D, ny, nx, Ly, Lx;
+  int T;               // output rows: T text rows, then the image tokens
   int64_t BH;
   int ys[kMaxAxisWindows], xs[kMaxAxisWindows];
 };
@@ -731,7 +737,7 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* 
         uint2 pk;
         pk.x = (unsigned)f2bf(acc.x * inv) | ((unsigned)f2bf(acc.y * inv) << 16);
         pk.y = (unsigned)f2bf(acc.z * inv) | ((unsigned)f2bf(acc.w * inv) << 16);
-        *reinterpret_cast<uint2*>(out + (bh * N + p) * b.D + 4 * d4) = pk;
+        *reinterpret_cast<uint2*>(out + (bh * (N + b.T) + b.T + p) * b.D + 4 * d4) = pk;
       }
     }
     __syncthreads();
@@ -782,8 +788,8 @@ int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, s
   return check_launch("vt_kernel");
 }
 
-int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH, int Nq, int Nk,
-                      int D, stream_t s) {
+int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH, int Nq, int q0,
+                      int q_rows, int Nk, int D, stream_t s) {
   AttnArgs a = {};
   a.q = (const u16*)q_rot;
   a.k = (const u16*)k_rot;
@@ -791,11 +797,14 @@ int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void
   a.out = (u16*)out;
   a.BH = BH;
   a.Nq = Nq;
+  a.q0 = q0;
+  a.q_rows = q_rows;
   a.k_rows = Nk;
   a.k_tiles = (Nk + BN - 1) / BN;
   a.n_kv = Nk;
   a.n_qtiles = (Nq + kAttnBM - 1) / kAttnBM;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
+  if (Nq == 0) return AREA_OK;
   return launch_attn<false>(a, D, (int64_t)a.n_qtiles * BH, (hipStream_t)s);
 }
 
@@ -812,8 +821,8 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   const int R = bridge_idx ? w.R : 0;
   if (w.BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
   ItemsWs iw = make_items_ws(ws.items, w.max_windows, n_base, w.max_items);
-  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(256), 0, st, plan, iw, kAttnBM, R, w.max_windows, w.max_items,
-                     w.max_gtiles);
+  hipLaunchKernelGGL(items_kernel, dim3(1), dim3(256), 0, st, plan, iw, kAttnBM, R + w.T, w.max_windows,
+                     w.max_items, w.max_gtiles);
   int rc = check_launch("items_kernel");
   if (rc) return rc;
   if (R > 0) {
@@ -827,11 +836,11 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   if (w.D == 128)
     hipLaunchKernelGGL((gather_kernel<128>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
                        (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
-                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.Gw, N, w.BH);
+                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N, w.BH);
   else
     hipLaunchKernelGGL((gather_kernel<64>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
                        (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
-                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.Gw, N, w.BH);
+                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N, w.BH);
   rc = check_launch("gather_kernel");
   if (rc) return rc;
   AttnArgs a = {};
@@ -841,6 +850,9 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   a.out = (u16*)out;
   a.BH = w.BH;
   a.Nq = N;
+  a.q0 = w.T;
+  a.q_rows = w.T + N;
+  a.T = w.T;
   a.k_rows = w.max_gtiles * BN;
   a.k_tiles = w.max_gtiles;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)w.D));
@@ -865,6 +877,7 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   b.nx = w.nx;
   b.Ly = w.Ly;
   b.Lx = w.Lx;
+  b.T = w.T;
   b.BH = w.BH;
   for (int i = 0; i < kMaxAxisWindows; ++i) {
     b.ys[i] = w.ys[i];

@@ -81,24 +81,25 @@ __device__ inline void rope8(float* x, int c, int D, float py, float px, const I
   }
 }
 
-// Attention operand preparation, one thread per 8 channels of a token:
-//   qo = RoPE(q) and ko = RoPE(k) at positions (row / div, col / div),
-//   vo = v, all written as IEEE fp16 (the MFMA operand type of the
-// attention kernels; bf16 -> fp16 is exact in fp16's normal range and the
-// rotated values keep three more mantissa bits than bf16 would).  k / v may
-// be null to skip them.
+// Attention operand preparation, one thread per 8 channels of a token of
+// the joint sequence (T text tokens, then the image grid):
+//   qo = RoPE(q) and ko = RoPE(k) at positions (row / div, col / div) for
+// image tokens and (0, 0) -- no rotation -- for text tokens, vo = v, all
+// written as IEEE fp16 (the MFMA operand type of the attention kernels;
+// bf16 -> fp16 is exact in fp16's normal range and the rotated values keep
+// three more mantissa bits than bf16 would).  k / v may be null to skip them.
 __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                    const uint4* __restrict__ v, uint4* __restrict__ qo,
                                                    uint4* __restrict__ ko, uint4* __restrict__ vo,
-                                                   int64_t total_chunks, int N, int Gw, int D, float div,
+                                                   int64_t total_chunks, int L, int T, int Gw, int D, float div,
                                                    InvFreq f) {
   int cpt = D / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
        i += (int64_t)gridDim.x * blockDim.x) {
     int c = (int)(i % cpt);
-    int n = (int)((i / cpt) % N);
-    float py = (float)(n / Gw) / div;
-    float px = (float)(n % Gw) / div;
+    int n = (int)((i / cpt) % L) - T;
+    float py = n < 0 ? 0.0f : (float)(n / Gw) / div;
+    float px = n < 0 ? 0.0f : (float)(n % Gw) / div;
     float x[8];
     unpack8(q[i], x);
     rope8(x, c, D, py, px, f);
@@ -115,30 +116,39 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, 
   }
 }
 
-// Pooled keys/values: one thread per (batch*head, pooled token, 8 channels).
-// Mean mode sums the block's f*f tokens in fp32 (block rows in order, then
-// columns) and divides by f*f; centre mode takes token (f/2, f/2) of the
-// block.  Keys are then rotated at the coarse position (by, bx); values are
-// not rotated.  One rounding at the end, to fp16 (the attention MFMA
-// operand type).
+// Pooled keys/values: one thread per (batch*head, output row, 8 channels).
+// The first T output rows are the text keys and values, copied unpooled and
+// unrotated (text sits at position (0, 0)).  For a pooled row, mean mode
+// sums the block's f*f tokens in fp32 (block rows in order, then columns)
+// and divides by f*f; centre mode takes token (f/2, f/2) of the block.  Keys
+// are then rotated at the coarse position (by, bx); values are not rotated.
+// One rounding at the end, to fp16 (the attention MFMA operand type).
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                    uint4* __restrict__ kp, uint4* __restrict__ vp,
                                                    int64_t total_chunks, int Gh, int Gw, int D, int f,
-                                                   int mode, InvFreq fr) {
+                                                   int mode, int T, InvFreq fr) {
   int cpt = D / 8;
   int Wp = Gw / f, Hp = Gh / f;
   int64_t Np = (int64_t)Hp * Wp;
-  int64_t N = (int64_t)Gh * Gw;
+  int64_t L = T + (int64_t)Gh * Gw;   // input rows per (batch, head)
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
        i += (int64_t)gridDim.x * blockDim.x) {
     int c = (int)(i % cpt);
     int64_t t = i / cpt;
-    int np = (int)(t % Np);
-    int64_t bh = t / Np;
-    int by = np / Wp, bx = np % Wp;
-    const uint4* kb = k + bh * N * cpt + c;
-    const uint4* vb = v + bh * N * cpt + c;
+    int64_t r = t % (T + Np);
+    int64_t bh = t / (T + Np);
     float ks[8], vs[8];
+    if (r < T) {
+      unpack8(k[(bh * L + r) * cpt + c], ks);
+      unpack8(v[(bh * L + r) * cpt + c], vs);
+      kp[i] = pack8_f16(ks);
+      vp[i] = pack8_f16(vs);
+      continue;
+    }
+    int np = (int)(r - T);
+    int by = np / Wp, bx = np % Wp;
+    const uint4* kb = k + (bh * L + T) * cpt + c;
+    const uint4* vb = v + (bh * L + T) * cpt + c;
     if (mode == AREA_POOL_CENTER) {
       int64_t n = (int64_t)(by * f + f / 2) * Gw + (bx * f + f / 2);
       unpack8(kb[n * cpt], ks);
@@ -221,22 +231,23 @@ int check_launch(const char* what) {
 }  // namespace
 
 int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
-                int Gh, int Gw, int D, float theta, float div, stream_t s) {
-  int64_t total = BH * (int64_t)Gh * Gw * (D / 8);
+                int T, int Gh, int Gw, int D, float theta, float div, stream_t s) {
+  const int L = T + Gh * Gw;
+  int64_t total = BH * (int64_t)L * (D / 8);
   InvFreq f = make_inv_freq(D, theta);
   hipLaunchKernelGGL(prep_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)s, (const uint4*)q,
-                     (const uint4*)k, (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, total, Gh * Gw, Gw,
+                     (const uint4*)k, (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, total, L, T, Gw,
                      D, div, f);
   return check_launch("prep_kernel");
 }
 
-int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int Gh, int Gw, int D,
+int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw, int D,
                 int f, int mode, float theta, stream_t s) {
-  int64_t total = BH * (int64_t)(Gh / f) * (Gw / f) * (D / 8);
+  int64_t total = BH * ((int64_t)T + (int64_t)(Gh / f) * (Gw / f)) * (D / 8);
   InvFreq fr = make_inv_freq(D, theta);
   hipLaunchKernelGGL(pool_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)s,
                      (const uint4*)k, (const uint4*)v, (uint4*)kp, (uint4*)vp, total, Gh, Gw, D, f,
-                     mode, fr);
+                     mode, T, fr);
   return check_launch("pool_kernel");
 }
 

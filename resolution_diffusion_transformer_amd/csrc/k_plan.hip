@@ -239,7 +239,7 @@ BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
 // consecutive threads cover one 128-channel row.
 template <int D>
 __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict__ k, long long* __restrict__ part,
-                                                         int N) {
+                                                         int N, int T) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int RPP = 256 / CPR;         // rows per pass
   __shared__ long long red[RPP][D];
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict
   int c = threadIdx.x % CPR, rr = threadIdx.x / CPR;
   long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int r0 = chunk * kBridgeChunk, r1 = min(N, r0 + kBridgeChunk);
-  const uint4* base = k + bh * (int64_t)N * CPR;
+  const uint4* base = k + (bh * (int64_t)(T + N) + T) * CPR;  // the image rows of the sequence
   for (int r = r0 + rr; r < r1; r += RPP) {
     uint4 w = base[(int64_t)r * CPR + c];
     const unsigned u[4] = {w.x, w.y, w.z, w.w};
@@ -287,7 +287,7 @@ __global__ void bridge_mean_kernel(const long long* __restrict__ part, double* _
 template <int D>
 __global__ __launch_bounds__(256) void bridge_cell_kernel(const unsigned short* __restrict__ k,
                                                           const double* __restrict__ mean, int* __restrict__ cell_out,
-                                                          int Gh, int Gw, int rh, int rw) {
+                                                          int Gh, int Gw, int rh, int rw, int T) {
 #pragma clang fp contract(off)
   __shared__ double mu[D];
   __shared__ double best_s[4];
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void bridge_cell_kernel(const unsigned short* 
   int x0 = (int)((int64_t)c * Gw / rw), x1 = (int)((int64_t)(c + 1) * Gw / rw);
   int cw = x1 - x0;
   int ncell = (y1 - y0) * cw;
-  const unsigned short* kb = k + bh * (int64_t)Gh * Gw * D;
+  const unsigned short* kb = k + (bh * ((int64_t)Gh * Gw + T) + T) * D;  // the image rows of the sequence
   double bs = -1.0;
   int bi = 0x7FFFFFFF;
   for (int i = threadIdx.x; i < ncell; i += blockDim.x) {
@@ -418,7 +418,7 @@ size_t bridge_ws_bytes(int64_t BH, int N, int D, int R) {
          align_up(sizeof(int) * BH * R);
 }
 
-int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D, int R, int rh, int rw,
+int launch_bridge(const void* k, int32_t* idx, int64_t BH, int T, int Gh, int Gw, int D, int R, int rh, int rw,
                   void* ws, stream_t s) {
   hipStream_t st = (hipStream_t)s;
   int N = Gh * Gw;
@@ -426,9 +426,11 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D
   int nch = n_chunks(N);
   if (BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
   if (D == 128)
-    hipLaunchKernelGGL(bridge_sum_kernel<128>, dim3(nch, (unsigned)BH), dim3(256), 0, st, (const uint4*)k, b.part, N);
+    hipLaunchKernelGGL(bridge_sum_kernel<128>, dim3(nch, (unsigned)BH), dim3(256), 0, st, (const uint4*)k, b.part, N,
+                       T);
   else
-    hipLaunchKernelGGL(bridge_sum_kernel<64>, dim3(nch, (unsigned)BH), dim3(256), 0, st, (const uint4*)k, b.part, N);
+    hipLaunchKernelGGL(bridge_sum_kernel<64>, dim3(nch, (unsigned)BH), dim3(256), 0, st, (const uint4*)k, b.part, N,
+                       T);
   int rc = check_launch("bridge_sum_kernel");
   if (rc) return rc;
   hipLaunchKernelGGL(bridge_mean_kernel, dim3((unsigned)BH), dim3(128), 0, st, (const long long*)b.part, b.mean,
@@ -437,10 +439,10 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int Gh, int Gw, int D
   if (rc) return rc;
   if (D == 128)
     hipLaunchKernelGGL(bridge_cell_kernel<128>, dim3(R, (unsigned)BH), dim3(256), 0, st, (const unsigned short*)k,
-                       (const double*)b.mean, b.cell, Gh, Gw, rh, rw);
+                       (const double*)b.mean, b.cell, Gh, Gw, rh, rw, T);
   else
     hipLaunchKernelGGL(bridge_cell_kernel<64>, dim3(R, (unsigned)BH), dim3(256), 0, st, (const unsigned short*)k,
-                       (const double*)b.mean, b.cell, Gh, Gw, rh, rw);
+                       (const double*)b.mean, b.cell, Gh, Gw, rh, rw, T);
   rc = check_launch("bridge_cell_kernel");
   if (rc) return rc;
   if (rw > kBridgeSortMax || rh > 65535) return fail(AREA_E_UNSUPPORTED, "bridge cell grid too large");

@@ -125,7 +125,7 @@ def test_gated_canvas_keeps_full_attention():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(D=96), -3), (dict(T=4), -3), (dict(Gh=127), -2), (dict(Gh=130, Gw=126), 0),
+    (dict(D=96), -3), (dict(T=4), 0), (dict(T=-1), -1), (dict(Gh=127), -2), (dict(Gh=130, Gw=126), 0),
     (dict(Gh=2 * 67, Gw=2 * 71), 0),               # both even: they share the factor 2
     (dict(w_start=60, w_min=64), -2), (dict(w_min=63), -2), (dict(bridge_k=3 * 1024 * 1024), -2),
     (dict(pool_mode=7), -1), (dict(split_den=0), -1), (dict(halo=-1), -1), (dict(B=0), -1),

@@ -59,6 +59,7 @@ class Workload:
     C: int = 16
     rope_theta: float = 10000.0
     seed: int = 0         # plan seed (window-boundary jitter)
+    T: int = 0            # text tokens ahead of the image tokens in every sequence
 
     @property
     def N(self) -> int:
@@ -87,6 +88,14 @@ WORKLOADS = {
                                native_w=83, dtype="bf16", p1_steps=20, f_min=2, p2_steps=16,
                                w_start=128, w_min=64, halo=4, bridge_k=256,
                                latent_kind="row_bands32"),
+    # Joint text + image sequences: the tiny grid with 8 text tokens, and FLUX.1 at
+    # 2048^2 with the 512 text tokens of its T5 prompt encoding.
+    "tiny-32-text": Workload("tiny-32-text", B=1, H=2, D=64, Gh=32, Gw=32, native_h=16, native_w=16,
+                             dtype="fp32", p1_steps=8, f_min=2, p2_steps=4, w_start=16, w_min=8,
+                             halo=1, bridge_k=16, latent_kind="tiny_patches", T=8),
+    "flux-2048-text": Workload("flux-2048-text", B=1, H=24, D=128, Gh=128, Gw=128, native_h=64, native_w=64,
+                               dtype="bf16", p1_steps=8, f_min=2, p2_steps=8, w_start=128, w_min=64,
+                               halo=4, bridge_k=256, latent_kind="half_columns", T=512),
 }
 
 
@@ -129,7 +138,8 @@ def _smooth_noise(n_img: int, Gh: int, Gw: int, gen, device, chunk: int = 1024):
 
 
 def make_qkv(wl: Workload, device: str = "cpu", dtype: Optional[str] = None, seed: int = 0):
-    """Return (q, k, v) torch tensors [B, H, N, D] on `device`.
+    """Return (q, k, v) torch tensors [B, H, T + N, D] on `device`: T text
+    tokens (iid N(0,1) rows, their own stream) ahead of the N image tokens.
 
     dtype "bf16" rounds to torch.bfloat16; "fp32" keeps float32.  The draw is
     reproducible per (device type, seed, workload)."""
@@ -141,6 +151,12 @@ def make_qkv(wl: Workload, device: str = "cpu", dtype: Optional[str] = None, see
         gen.manual_seed(seed * 1000003 + which)
         f = _smooth_noise(wl.B * wl.H * wl.D, wl.Gh, wl.Gw, gen, device)
         f = f.view(wl.B, wl.H, wl.D, wl.N).transpose(2, 3).contiguous()
+        if wl.T > 0:
+            gt = torch.Generator(device=device)
+            gt.manual_seed(seed * 1000003 + which + 100)
+            t = torch.randn((wl.B, wl.H, wl.T, wl.D), generator=gt, device=device, dtype=torch.float32)
+            f = torch.cat([t, f], dim=2)
+            del t
         outs.append(f.to(torch.bfloat16) if dtype == "bf16" else f)
         del f
     return tuple(outs)
