@@ -18,7 +18,8 @@ int fail(int status, const std::string& msg);
 // ------------------------------------------------------- fixed constants --
 constexpr int kMaxAxisWindows = 64;    // base windows per axis (kernel-argument table)
 constexpr int kAttnQG = 1;             // 32-query groups per attention wave
-constexpr int kAttnBM = 128 * kAttnQG; // queries per attention work item (4 waves)
+constexpr int kAttnWaves = 8;          // waves per attention work-group
+constexpr int kAttnBM = 32 * kAttnQG * kAttnWaves;  // queries per attention work item
 constexpr int kAttnBN = 64;            // keys per staged tile
 constexpr int kBridgeChunk = 1024;     // rows per partial mean-key sum
 constexpr size_t kAlign = 256;

@@ -17,13 +17,19 @@
 //    v_permlane32_swap with the partner lane.  K rows sit in LDS in the
 //    order that makes the S^T accumulator registers the fp16 B operand of
 //    O^T += V^T P^T, so P never leaves registers.
-//  * K and V^T tiles reach LDS by global->LDS DMA (global_load_lds_dwordx4,
-//    no register staging), double-buffered: the next tile's DMA runs under
-//    the current tile's compute; one barrier per tile.  Rows are unpadded and
-//    the 16-byte chunks XOR-swizzled by row, so the 128-bit MFMA operand
-//    reads are bank-conflict free.  Four waves of 32 queries use ~230 VGPRs,
-//    so two work-groups share a CU and overlap each other's softmax (VALU)
-//    and MFMA phases.
+//  * K and V^T tiles reach LDS by global->LDS DMA (buffer_load ... lds, no
+//    register staging), double-buffered and one barrier per tile.  Rows are
+//    unpadded and the 16-byte chunks XOR-swizzled by row, so the 128-bit
+//    MFMA operand reads are bank-conflict free.
+//  * Each wave runs a two-phase software pipeline over key tiles: the
+//    matrix cores compute the scores of tile j+1 while the VALU turns the
+//    scores of tile j into P (exp2, fp16), then they compute O += P V for
+//    tile j while the VALU sums P and takes the maximum of tile j+1.
+//    sched_group_barrier interleaves the two instruction streams, so the
+//    softmax runs in the shadow of the MFMAs instead of after them.
+//  * Eight waves of 32 queries (256 queries per work-group) use ~230
+//    VGPRs: one work-group per CU, two waves per SIMD, and one K/V tile DMA
+//    serves 256 queries.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
 //    only moves when a score exceeds it by more than 2^8.
 //  * Work items are mapped XCD-aware: consecutive items (same head, same
@@ -343,38 +349,51 @@ __device__ __attribute__((always_inline)) inline int key_perm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-// Issue the DMA of tile `tile` into one LDS stage: K rows then V^T rows,
-// CH 16-byte chunks of each per thread.  Rows past the last key of the set
-// re-read the last key (their scores are masked).  `wave` is wave-uniform, so
-// the LDS addresses (M0) are scalar; global addresses are a scalar tile base
-// plus a 32-bit lane offset.
+// Work-group of the attention kernel: kAttnWaves waves of 32 kAttnQG queries.
+constexpr int kThreads = 64 * kAttnWaves;
+
+// DMA of one tile's K rows (issue_k) or V^T rows (issue_v) into an LDS
+// stage, CH 16-byte chunks per thread, with buffer loads: a per-tile buffer
+// resource (scalar base and byte count) plus a loop-invariant lane offset.
+// K rows past the last key of the set fall outside the resource's range and
+// read as zero (their scores are masked).  `wave` is wave-uniform, so the LDS
+// addresses (M0) are scalar.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int D>
-__device__ __attribute__((always_inline)) inline void issue_tile(u16* ks, u16* vt, int tile, int tid, int wave,
-                                                                 int nkv, const u16* kbase, const u16* vtbase) {
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int VCH = BN / 8;         // 16-byte chunks per V^T row
-  constexpr int CH = BN * D / 8 / 256;
-  const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)tile * BN * D);
-  const char* vtt = reinterpret_cast<const char*>(vtbase + (int64_t)tile * D * BN);
-  const int last = nkv - 1 - tile * BN;
+__device__ __attribute__((always_inline)) inline void issue_k(u16* ks, int tile, int tid, int wave, int nkv,
+                                                              const u16* kbase) {
+  constexpr int KCH = D / 8;  // 16-byte chunks per K row
+  constexpr int CH = BN * D / 8 / kThreads;
+  const int rows = __builtin_amdgcn_readfirstlane(min(max(nkv - tile * BN, 0), BN));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)tile * BN * D), (short)0, rows * D * 2, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int p = i * 256 + tid;      // LDS chunk written by this lane
+    const int p = i * kThreads + tid;  // LDS chunk written by this lane
     const int r = p / KCH, pc = p - r * KCH;
     const int c = pc ^ swz<D * 2>(r);
-    const unsigned off = (unsigned)(min(key_perm(r), last) * (D * 2) + c * 16);
-    __builtin_amdgcn_global_load_lds((gptr_t)(kt + off), (lptr_t)(ks + (i * 256 + wave * 64) * 8), 16, 0, 0);
+    const unsigned off = (unsigned)(key_perm(r) * (D * 2) + c * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(ks + (i * kThreads + wave * 64) * 8), 16, off, 0, 0, 0);
   }
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void issue_v(u16* vt, int tile, int tid, int wave,
+                                                              const u16* vtbase) {
+  constexpr int VCH = BN / 8;  // 16-byte chunks per V^T row
+  constexpr int CH = BN * D / 8 / kThreads;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vtbase + (int64_t)tile * D * BN), (short)0, D * BN * 2, kBufferWord3);
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int p = i * 256 + tid;
+    const int p = i * kThreads + tid;
     const int d = p / VCH, pc = p - d * VCH;
     const int c = pc ^ swz<BN * 2>(d);
     const unsigned off = (unsigned)(d * (BN * 2) + c * 16);
-    __builtin_amdgcn_global_load_lds((gptr_t)(vtt + off), (lptr_t)(vt + (i * 256 + wave * 64) * 8), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(vt + (i * kThreads + wave * 64) * 8), 16, off, 0, 0, 0);
   }
 }
 
@@ -403,35 +422,18 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&s)[QG
   }
 }
 
-// O^T += V^T P^T for one tile.
-template <int D, int QG>
-__device__ __attribute__((always_inline)) inline void tile_pv(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
-                                                              const f16x8 (&pf)[QG][4]) {
-  const int sw = swz<BN * 2>(n);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const u16* vr = vt + (32 * db + n) * BN + (((2 * ks + hi) ^ sw) * 8);
-      f16x8 af = *reinterpret_cast<const f16x8*>(vr);
-#pragma unroll
-      for (int g = 0; g < QG; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, pf[g][ks], o[g][db], 0, 0, 0);
-    }
-  }
-}
-
 // Keys at or beyond `valid` (tail of the last tile) get a -inf score.  S^T
 // register 8*jj + i of block kb is key 32 kb + 16 jj + 8 hi + i.
 template <int QG>
 __device__ __attribute__((always_inline)) inline void mask_tail(f32x16 (&s)[QG][2], int valid, int hi) {
+  const int lim = valid - 8 * hi;
 #pragma unroll
   for (int g = 0; g < QG; ++g)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int key = 32 * kb + 16 * (i >> 3) + 8 * hi + (i & 7);
-        s[g][kb][i] = key < valid ? s[g][kb][i] : -INFINITY;
+        s[g][kb][i] = 32 * kb + 16 * (i >> 3) + (i & 7) < lim ? s[g][kb][i] : -INFINITY;
       }
 }
 
@@ -447,12 +449,11 @@ __device__ __attribute__((always_inline)) inline float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Online softmax of one tile (exp2 units, lazy maximum): P^T in fp16,
-// running sums updated, per-group rescale factors of O returned.
+// Running maximum after one more tile (exp2 units, lazy: it only moves when
+// a score exceeds it by more than 2^kLazy); alpha = factor for O and l.
 template <int QG>
-__device__ __attribute__((always_inline)) inline void tile_softmax(const f32x16 (&s)[QG][2], float c,
-                                                                   float (&m_run)[QG], float (&l_run)[QG],
-                                                                   float (&alpha)[QG], f16x8 (&pf)[QG][4]) {
+__device__ __attribute__((always_inline)) inline void tile_max(const f32x16 (&s)[QG][2], float c,
+                                                               float (&m_run)[QG], float (&alpha)[QG]) {
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     float mx = fmaxf(s[g][0][0], s[g][0][1]);
@@ -465,7 +466,17 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(const f32x16 
     const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
     alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
     m_run[g] = m_new;
-    const float negm = -m_new;
+  }
+}
+
+// P^T = exp2(c s - m) in fp16 and its in-lane row sums.
+template <int QG>
+__device__ __attribute__((always_inline)) inline void tile_exp(const f32x16 (&s)[QG][2], float c,
+                                                               const float (&m_run)[QG], float (&lsum)[QG],
+                                                               f16x8 (&pf)[QG][4]) {
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    const float negm = -m_run[g];
     float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -481,19 +492,157 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(const f32x16 
         pf[g][2 * kb + hh] = pv;
       }
     }
-    l_run[g] = l_run[g] * alpha[g] + (ls0 + ls1);
+    lsum[g] = ls0 + ls1;
   }
 }
 
+// Operand fragments are read from LDS kFragAhead MFMAs before their use;
+// each MFMA of phase A is paired with kValuA VALU instructions of the
+// softmax (per two scores), each MFMA of phase B with kValuB.
+constexpr int kFragAhead = 3;
+constexpr int kValuA = 5;
+constexpr int kValuB = 3;
+
+// sched_group_barrier masks
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+__device__ __attribute__((always_inline)) inline const u16* uniform_ptr(const u16* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (const u16*)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage, int elem_off) {
+  return *reinterpret_cast<const f16x8*>(stage + elem_off);
+}
+
+// Phase A of one step: S^T of the next tile for the wave's QG query groups
+// (2 D/16 K fragments, each read once from LDS and used by every group)
+// while the VALU turns the current scores into fp16 P^T.
+template <int D, int QG>
+__device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2], const u16* ks, int n, int hi,
+                                                              const f16x8 (&qf)[QG][D / 16],
+                                                              const f32x16 (&sc)[QG][2], float c,
+                                                              const float (&negm)[QG], f16x8 (&pf)[QG][4]) {
+  constexpr int NT = 2 * (D / 16);
+  constexpr int EPM = 32 * QG / NT;  // scores turned into P per fragment
+  constexpr int PF = kFragAhead;
+  const int sw = swz<D * 2>(n);
+  auto koff = [&](int j) __attribute__((always_inline)) {
+    const int kd = j >> 1, kb = j & 1;
+    return (32 * kb + n) * D + (((2 * kd + hi) ^ sw) * 8);
+  };
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[g][kb][i] = 0.0f;
+  f16x8 fr[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fr[j] = lds_frag(ks, koff(j));
+  _Float16 ph[QG][32];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const f16x8 f = fr[j % PF];
+    if (j + PF < NT) fr[j % PF] = lds_frag(ks, koff(j + PF));
+#pragma unroll
+    for (int g = 0; g < QG; ++g)
+      sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], sn[g][j & 1], 0, 0, 0);
+#pragma unroll
+    for (int e = EPM * j; e < EPM * j + EPM; ++e) {
+      const int g = e >> 5, x = e & 31;
+      ph[g][x] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[g][x >> 4][x & 15], c, negm[g]));
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[g][r][i] = ph[g][8 * r + i];
+  // issue order: the first PF reads, then per fragment its MFMAs, the next
+  // read and the VALU work of EPM scores
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
+    if (j + PF < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuA * EPM / 2, 0);
+  }
+}
+
+// Phase B of one step: O^T += V^T P^T for every group (4 D/32 V^T
+// fragments, each read once) while the VALU sums P and takes the next
+// tile's per-lane maxima.
+template <int D, int QG>
+__device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
+                                                              const f16x8 (&pf)[QG][4], const f32x16 (&sn)[QG][2],
+                                                              float (&psum)[QG], float (&mx)[QG]) {
+  constexpr int DB = D / 32;
+  constexpr int NT = 4 * DB;
+  constexpr int PF = kFragAhead;
+  const int sw = swz<BN * 2>(n);
+  auto voff = [&](int j) __attribute__((always_inline)) {
+    const int ks = j / DB, db = j % DB;
+    return (32 * db + n) * BN + (((2 * ks + hi) ^ sw) * 8);
+  };
+  f16x8 fr[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fr[j] = lds_frag(vt, voff(j));
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const f16x8 f = fr[j % PF];
+    if (j + PF < NT) fr[j % PF] = lds_frag(vt, voff(j + PF));
+#pragma unroll
+    for (int g = 0; g < QG; ++g)
+      o[g][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, pf[g][j / DB], o[g][j % DB], 0, 0, 0);
+  }
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        s0 = __builtin_amdgcn_fdot2(h2{pf[g][r][i], pf[g][r][i + 1]}, one2, s0, false);
+        s1 = __builtin_amdgcn_fdot2(h2{pf[g][r][i + 2], pf[g][r][i + 3]}, one2, s1, false);
+      }
+    psum[g] = s0 + s1;
+    float m = fmaxf(sn[g][0][0], sn[g][0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, sn[g][kb][i]);
+    mx[g] = m;
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
+    if (j + PF < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuB * QG, 0);
+  }
+}
+
+// Work-groups per CU the register budget is sized for: two four-wave groups,
+// else one.
+constexpr int kAttnGroupsPerCu = kAttnQG == 1 && kAttnWaves == 4 ? 2 : 1;
+
 template <int D, bool WIN>
-__global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const AttnArgs a) {
   constexpr int QG = kAttnQG;     // 32-query groups per wave
   constexpr int BM = kAttnBM;     // 4 waves x QG groups x 32 queries
   constexpr int KD = D / 16;
   constexpr int DB = D / 32;
   constexpr int K_ELEMS = BN * D;
   constexpr int V_ELEMS = D * BN;
-  static_assert(BM == 4 * 32 * QG, "query tile");
+  static_assert(BM == kAttnWaves * 32 * QG, "query tile");
 
   // two LDS stages, as separate objects so that the compiler can tell a DMA
   // into one stage from reads of the other
@@ -574,15 +723,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[g][db][i] = 0.0f;
   }
 
-  // One tile: scores, softmax, O update.
-  auto compute = [&](const u16* ks, const u16* vt, int j) __attribute__((always_inline)) {
-    f32x16 sc[QG][2];
-    tile_scores<D, QG>(sc, ks, n, hi, qf);
-    const int valid = nkv - j * BN;
-    if (valid < BN) mask_tail<QG>(sc, valid, hi);
-    float alpha[QG];
-    f16x8 pf[QG][4];
-    tile_softmax<QG>(sc, c, m_run, l_run, alpha, pf);
+  float alpha[QG];
+  // Software pipeline over key tiles: while the matrix cores compute the
+  // scores of tile j+1, the VALU turns the scores of tile j into P; while
+  // they compute O += P V for tile j, the VALU sums P and takes the maximum
+  // of tile j+1.  K tile j+1 and V tile j are resident during step j; K tile
+  // j+2 and V tile j+1 stream into the other stages meanwhile.
+  auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j)
+      __attribute__((always_inline)) {
     bool resc = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) resc |= alpha[g] != 1.0f;
@@ -594,28 +742,59 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(const AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha[g];
     }
-    tile_pv<D, QG>(o, vt, n, hi, pf);
+    f16x8 pf[QG][4];
+    float negm[QG];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) negm[g] = -m_run[g];
+    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, c, negm, pf);
+    // keep P's computation in this block: its only use is after the branch
+#pragma unroll
+    for (int g = 0; g < QG; ++g) asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]));
+    const int valid = nkv - (j + 1) * BN;
+    if (valid < BN) mask_tail<QG>(snext, valid, hi);
+    float psum[QG], mx[QG];
+    phase_b<D, QG>(o, vtc, n, hi, pf, snext, psum, mx);
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      l_run[g] = l_run[g] * alpha[g] + psum[g];
+      const float mc = pair_max(mx[g]) * c;
+      const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
+      alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+    }
   };
 
-  // Tile j lives in stage j % 2.  Each half-iteration starts the DMA of the
-  // next tile into the other stage, computes tile j, then waits for its own
-  // DMAs and syncs: the next tile has landed for every wave and stage j % 2
-  // is free.  No DMA is outstanding at a branch merge, which keeps the
-  // compiler's LDS-DMA wait tracking exact (no wait before reading a stage).
-  // The last half-iteration re-loads the last tile into the idle stage
-  // instead of branching around the DMA.
+  // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each
+  // half-iteration first starts the DMAs into the two free stages, then
+  // computes, then waits for its own DMAs and syncs.  No DMA is outstanding
+  // at a branch merge; the last half-iteration re-loads clamped tiles instead
+  // of branching around the DMA, and its scores of the tile past the end are
+  // never used.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  issue_tile<D>(ks0, vt0, 0, tid, wave_u, nkv, kbase, vtbase);
+  // the buffer resources below need wave-uniform bases and sizes
+  kbase = uniform_ptr(kbase);
+  vtbase = uniform_ptr(vtbase);
+  nkv = __builtin_amdgcn_readfirstlane(nkv);
+  f32x16 sa[QG][2], sb[QG][2];
+  issue_k<D>(ks0, 0, tid, wave_u, nkv, kbase);
+  issue_v<D>(vt0, 0, tid, wave_u, vtbase);
+  issue_k<D>(ks1, min(1, nt - 1), tid, wave_u, nkv, kbase);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
+  tile_scores<D, QG>(sa, ks0, n, hi, qf);
+  if (nkv < BN) mask_tail<QG>(sa, nkv, hi);
+  tile_max<QG>(sa, c, m_run, alpha);
+  __syncthreads();
   for (int j = 0; j < nt; j += 2) {
-    issue_tile<D>(ks1, vt1, min(j + 1, nt - 1), tid, wave_u, nkv, kbase, vtbase);
-    compute(ks0, vt0, j);
+    issue_k<D>(ks0, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
+    issue_v<D>(vt1, min(j + 1, nt - 1), tid, wave_u, vtbase);
+    step(sa, sb, ks1, vt0, j);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     if (j + 1 >= nt) break;
-    issue_tile<D>(ks0, vt0, min(j + 2, nt - 1), tid, wave_u, nkv, kbase, vtbase);
-    compute(ks1, vt1, j + 1);
+    issue_k<D>(ks1, min(j + 3, nt - 1), tid, wave_u, nkv, kbase);
+    issue_v<D>(vt0, min(j + 2, nt - 1), tid, wave_u, vtbase);
+    step(sb, sa, ks0, vt1, j + 1);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
   }
@@ -757,9 +936,9 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
     if (e != hipSuccess) return fail(AREA_E_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
   }
   if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, WIN>), grid, dim3(256), 0, st, b);
+    hipLaunchKernelGGL((attn_kernel<128, WIN>), grid, dim3(kThreads), 0, st, b);
   else
-    hipLaunchKernelGGL((attn_kernel<64, WIN>), grid, dim3(256), 0, st, b);
+    hipLaunchKernelGGL((attn_kernel<64, WIN>), grid, dim3(kThreads), 0, st, b);
   int rc = check_launch(WIN ? "attn_kernel<window>" : "attn_kernel<dense>");
   if (rc) return rc;
   if (ev.end) {
