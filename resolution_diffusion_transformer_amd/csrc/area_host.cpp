@@ -312,6 +312,7 @@ static WindowLayout window_layout(const area_problem& p) {
     off += align_up(bytes);
     return at;
   };
+  // rotated Q and K first, in the places the text pass of a step reads them
   l.q = take(tok_bytes(p));
   l.k = take(tok_bytes(p));
   l.slots = take((size_t)m.q_total * BH * p.D * 4);
@@ -562,6 +563,28 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
   return launch_dense_attn(qr, kr, vt, out, BH, L, 0, L, L, p->D, stream);
 }
 
+}  // extern "C"
+
+namespace area {
+
+// The text queries against every key, from rotated fp16 Q and K already at
+// the start of a full-attention-shaped workspace (Q rows at 0, K rows at the
+// next aligned offset): V^T after them, then dense attention over T queries.
+static int text_pass(const area_problem& p, char* ws, const void* v, void* out, void* stream) {
+  const int64_t BH = BH_of(p);
+  const int L = (int)L_of(p);
+  char* qr = ws;
+  char* kr = qr + align_up(tok_bytes(p));
+  char* vt = kr + align_up(tok_bytes(p));
+  int rc = launch_vt(v, vt, BH, L, p.D, true, stream);
+  if (rc) return rc;
+  return launch_dense_attn(qr, kr, vt, out, BH, p.T, 0, L, L, p.D, stream);
+}
+
+}  // namespace area
+
+extern "C" {
+
 int area_text_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out, void* ws,
                    size_t ws_bytes, void* stream) {
   int rc = validate(p);
@@ -570,16 +593,12 @@ int area_text_attn(const area_problem* p, const void* q, const void* k, const vo
   if (p->T == 0) return AREA_OK;
   rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
   if (rc) return rc;
-  int64_t BH = BH_of(*p);
-  const int L = (int)L_of(*p);
   char* qr = (char*)ws;
   char* kr = qr + align_up(tok_bytes(*p));
-  char* vt = kr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH_of(*p), p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
+                   stream);
   if (rc) return rc;
-  rc = launch_vt(v, vt, BH, L, p->D, true, stream);
-  if (rc) return rc;
-  return launch_dense_attn(qr, kr, vt, out, BH, p->T, 0, L, L, p->D, stream);
+  return text_pass(*p, qr, v, out, stream);
 }
 
 int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
@@ -718,8 +737,10 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       if (rc) return rc;
       rc = area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
                             ws_bytes - l.window_ws, stream);
-      if (rc) return rc;
-      return area_text_attn(p, q, k, v, out, base + l.window_ws, ws_bytes - l.window_ws, stream);
+      if (rc || p->T == 0) return rc;
+      // the windowed pass left rotated fp16 Q and K (text rows included) at
+      // the start of its workspace, where the text pass reads them
+      return text_pass(*p, base + l.window_ws, v, out, stream);
     }
   }
 }
