@@ -469,33 +469,6 @@ __device__ __attribute__((always_inline)) inline void tile_max(const f32x16 (&s)
   }
 }
 
-// P^T = exp2(c s - m) in fp16 and its in-lane row sums.
-template <int QG>
-__device__ __attribute__((always_inline)) inline void tile_exp(const f32x16 (&s)[QG][2], float c,
-                                                               const float (&m_run)[QG], float (&lsum)[QG],
-                                                               f16x8 (&pf)[QG][4]) {
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const float negm = -m_run[g];
-    float ls0 = 0.0f, ls1 = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f16x8 pv;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[g][kb][8 * hh + i], c, negm));
-          if (i & 1) ls1 += p; else ls0 += p;
-          pv[i] = (_Float16)p;
-        }
-        pf[g][2 * kb + hh] = pv;
-      }
-    }
-    lsum[g] = ls0 + ls1;
-  }
-}
-
 // Operand fragments are read from LDS kFragAhead MFMAs before their use;
 // each MFMA of phase A is paired with kValuA VALU instructions of the
 // softmax (per two scores), each MFMA of phase B with kValuB.
@@ -637,7 +610,7 @@ constexpr int kAttnGroupsPerCu = kAttnQG == 1 && kAttnWaves == 4 ? 2 : 1;
 template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const AttnArgs a) {
   constexpr int QG = kAttnQG;     // 32-query groups per wave
-  constexpr int BM = kAttnBM;     // 4 waves x QG groups x 32 queries
+  constexpr int BM = kAttnBM;     // kAttnWaves waves x QG groups x 32 queries
   constexpr int KD = D / 16;
   constexpr int DB = D / 32;
   constexpr int K_ELEMS = BN * D;
