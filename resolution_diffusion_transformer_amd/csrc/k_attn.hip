@@ -827,27 +827,29 @@ constexpr int kMaxCover = 8;
 __device__ inline int tent_w(int u, int L) { return min(u + 1, L - u); }
 
 // Tokens covered by more than one window: out = sum_w wt_w * O_w / wsum,
-// windows in record order.
+// windows in record order.  One block per kBlendTok tokens: the first
+// kBlendTok threads find their token's covering windows in parallel, then
+// the whole block writes the blended rows of the overlapped ones.
 __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* __restrict__ plan,
                                                     const int* __restrict__ rec_start, const int* __restrict__ slot_off,
                                                     const int32_t* __restrict__ wsum, const float* __restrict__ slots,
                                                     u16* __restrict__ out) {
-  __shared__ int s_slot[kMaxCover * kMaxCover];
-  __shared__ float s_wt[kMaxCover * kMaxCover];
-  __shared__ int s_cnt;
-  int64_t N = (int64_t)b.Gh * b.Gw;
-  int D4 = b.D / 4;
-  for (int k = 0; k < kBlendTok; ++k) {
-    int64_t p = (int64_t)blockIdx.x * kBlendTok + k;
-    if (p >= N) break;
-    int y = (int)(p / b.Gw), x = (int)(p % b.Gw);
-    if (threadIdx.x == 0) {
+  __shared__ int s_slot[kBlendTok][kMaxCover * kMaxCover];
+  __shared__ float s_wt[kBlendTok][kMaxCover * kMaxCover];
+  __shared__ int s_cnt[kBlendTok];
+  const int64_t N = (int64_t)b.Gh * b.Gw;
+  const int64_t p0 = (int64_t)blockIdx.x * kBlendTok;
+  if (threadIdx.x < kBlendTok) {
+    const int t = threadIdx.x;
+    const int64_t p = p0 + t;
+    int cnt = 0;
+    if (p < N) {
+      const int y = (int)(p / b.Gw), x = (int)(p % b.Gw);
       int iy[kMaxCover], ix[kMaxCover], cy = 0, cx = 0;
       for (int i = 0; i < b.ny; ++i)
         if (y >= b.ys[i] && y < b.ys[i] + b.Ly && cy < kMaxCover) iy[cy++] = i;
       for (int j = 0; j < b.nx; ++j)
         if (x >= b.xs[j] && x < b.xs[j] + b.Lx && cx < kMaxCover) ix[cx++] = j;
-      int cnt = 0;
       if (cy * cx > 1) {
         for (int a = 0; a < cy; ++a)
           for (int c = 0; c < cx; ++c) {
@@ -863,36 +865,39 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* 
             }
             const int32_t* wp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rr;
             int uy = y - wp[0], ux = x - wp[1];
-            s_wt[cnt] = (float)(tent_w(uy, wp[2]) * tent_w(ux, wp[3]));
-            s_slot[cnt] = slot_off[rr] + uy * wp[3] + ux;
+            s_wt[t][cnt] = (float)(tent_w(uy, wp[2]) * tent_w(ux, wp[3]));
+            s_slot[t][cnt] = slot_off[rr] + uy * wp[3] + ux;
             ++cnt;
           }
       }
-      s_cnt = cnt;
     }
-    __syncthreads();
-    int cnt = s_cnt;
-    if (cnt > 1) {
-      float inv = 1.0f / (float)wsum[p];
-      for (int e = threadIdx.x; e < b.BH * D4; e += blockDim.x) {
-        int64_t bh = e / D4;
-        int d4 = e - (int)bh * D4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int i = 0; i < cnt; ++i) {
-          float4 v = *reinterpret_cast<const float4*>(slots + ((int64_t)s_slot[i] * b.BH + bh) * b.D + 4 * d4);
-          float wgt = s_wt[i];
-          acc.x += wgt * v.x;
-          acc.y += wgt * v.y;
-          acc.z += wgt * v.z;
-          acc.w += wgt * v.w;
-        }
-        uint2 pk;
-        pk.x = (unsigned)f2bf(acc.x * inv) | ((unsigned)f2bf(acc.y * inv) << 16);
-        pk.y = (unsigned)f2bf(acc.z * inv) | ((unsigned)f2bf(acc.w * inv) << 16);
-        *reinterpret_cast<uint2*>(out + (bh * (N + b.T) + b.T + p) * b.D + 4 * d4) = pk;
-      }
+    s_cnt[t] = cnt;
+  }
+  __syncthreads();
+  const int D4 = b.D / 4;
+  const int64_t per_tok = b.BH * D4;
+  for (int64_t e = threadIdx.x; e < kBlendTok * per_tok; e += blockDim.x) {
+    const int t = (int)(e / per_tok);
+    const int cnt = s_cnt[t];
+    if (cnt <= 1) continue;
+    const int64_t r = e - t * per_tok;
+    const int64_t bh = r / D4;
+    const int d4 = (int)(r - bh * D4);
+    const int64_t p = p0 + t;
+    const float inv = 1.0f / (float)wsum[p];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < cnt; ++i) {
+      float4 v = *reinterpret_cast<const float4*>(slots + ((int64_t)s_slot[t][i] * b.BH + bh) * b.D + 4 * d4);
+      float wgt = s_wt[t][i];
+      acc.x += wgt * v.x;
+      acc.y += wgt * v.y;
+      acc.z += wgt * v.z;
+      acc.w += wgt * v.w;
     }
-    __syncthreads();
+    uint2 pk;
+    pk.x = (unsigned)f2bf(acc.x * inv) | ((unsigned)f2bf(acc.y * inv) << 16);
+    pk.y = (unsigned)f2bf(acc.z * inv) | ((unsigned)f2bf(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(out + (bh * (N + b.T) + b.T + p) * b.D + 4 * d4) = pk;
   }
 }
 

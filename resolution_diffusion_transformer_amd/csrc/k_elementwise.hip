@@ -3,6 +3,7 @@
 // Haar detail-energy map.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -63,21 +64,31 @@ __device__ inline uint4 pack8(const float* x) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Rotate the 8 channels [8c, 8c+8) of one token at grid position (py, px).
-// Channels below D/2 follow the row, the others the column; pair
-// (2k, 2k+1) of an axis half turns by pos * inv_freq[k].
-__device__ inline void rope8(float* x, int c, int D, float py, float px, const InvFreq& f) {
+// Rotation of the 8 channels [8c, 8c+8) of a token at grid position
+// (py, px): channels below D/2 follow the row, the others the column; pair
+// (2k, 2k+1) of an axis half turns by pos * inv_freq[k].  rope_cs computes
+// the four (cos, sin) pairs once, rope_apply turns one vector by them.
+struct Rot4 {
+  float co[4], sn[4];
+};
+
+__device__ inline Rot4 rope_cs(int c, int D, float py, float px, const InvFreq& f) {
+  Rot4 r;
   int d0 = 8 * c;
   int half = D / 2;
   float pos = d0 < half ? py : px;
   int k0 = (d0 % half) / 2;
 #pragma unroll
+  for (int j = 0; j < 4; ++j) sincosf(pos * f.v[k0 + j], &r.sn[j], &r.co[j]);
+  return r;
+}
+
+__device__ inline void rope_apply(float* x, const Rot4& r) {
+#pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float s, co;
-    sincosf(pos * f.v[k0 + j], &s, &co);
     float a = x[2 * j], b = x[2 * j + 1];
-    x[2 * j] = a * co - b * s;
-    x[2 * j + 1] = a * s + b * co;
+    x[2 * j] = a * r.co[j] - b * r.sn[j];
+    x[2 * j + 1] = a * r.sn[j] + b * r.co[j];
   }
 }
 
@@ -88,30 +99,42 @@ __device__ inline void rope8(float* x, int c, int D, float py, float px, const I
 // written as IEEE fp16 (the MFMA operand type of the attention kernels;
 // bf16 -> fp16 is exact in fp16's normal range and the rotated values keep
 // three more mantissa bits than bf16 would).  k / v may be null to skip them.
+// Grid: x over the (row, chunk) pairs of one (batch, head), y over (batch,
+// head), both grid-strided; D is a template parameter so the chunk split is
+// a shift.
+template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                    const uint4* __restrict__ v, uint4* __restrict__ qo,
-                                                   uint4* __restrict__ ko, uint4* __restrict__ vo,
-                                                   int64_t total_chunks, int L, int T, int Gw, int D, float div,
-                                                   InvFreq f) {
-  int cpt = D / 8;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int c = (int)(i % cpt);
-    int n = (int)((i / cpt) % L) - T;
-    float py = n < 0 ? 0.0f : (float)(n / Gw) / div;
-    float px = n < 0 ? 0.0f : (float)(n % Gw) / div;
-    float x[8];
-    unpack8(q[i], x);
-    rope8(x, c, D, py, px, f);
-    qo[i] = pack8_f16(x);
-    if (k) {
-      unpack8(k[i], x);
-      rope8(x, c, D, py, px, f);
-      ko[i] = pack8_f16(x);
-    }
-    if (v) {
-      unpack8(v[i], x);
-      vo[i] = pack8_f16(x);
+                                                   uint4* __restrict__ ko, uint4* __restrict__ vo, int64_t BH,
+                                                   int L, int T, int Gw, float div, InvFreq f) {
+  constexpr int CPT = D / 8;
+  const int64_t per_bh = (int64_t)L * CPT;
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < per_bh;
+         j += (int64_t)gridDim.x * blockDim.x) {
+      const int c = (int)(j & (CPT - 1));
+      const int n = (int)(j / CPT) - T;
+      float py = 0.0f, px = 0.0f;
+      if (n >= 0) {
+        const int yy = n / Gw;
+        py = (float)yy / div;
+        px = (float)(n - yy * Gw) / div;
+      }
+      const Rot4 r = rope_cs(c, D, py, px, f);
+      const int64_t i = bh * per_bh + j;
+      float x[8];
+      unpack8(q[i], x);
+      rope_apply(x, r);
+      qo[i] = pack8_f16(x);
+      if (k) {
+        unpack8(k[i], x);
+        rope_apply(x, r);
+        ko[i] = pack8_f16(x);
+      }
+      if (v) {
+        unpack8(v[i], x);
+        vo[i] = pack8_f16(x);
+      }
     }
   }
 }
@@ -123,62 +146,65 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, 
 // and divides by f*f; centre mode takes token (f/2, f/2) of the block.  Keys
 // are then rotated at the coarse position (by, bx); values are not rotated.
 // One rounding at the end, to fp16 (the attention MFMA operand type).
+// Grid as for prep_kernel: x over the (output row, chunk) pairs of one
+// (batch, head), y over (batch, head).
+template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                                   uint4* __restrict__ kp, uint4* __restrict__ vp,
-                                                   int64_t total_chunks, int Gh, int Gw, int D, int f,
-                                                   int mode, int T, InvFreq fr) {
-  int cpt = D / 8;
-  int Wp = Gw / f, Hp = Gh / f;
-  int64_t Np = (int64_t)Hp * Wp;
-  int64_t L = T + (int64_t)Gh * Gw;   // input rows per (batch, head)
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int c = (int)(i % cpt);
-    int64_t t = i / cpt;
-    int64_t r = t % (T + Np);
-    int64_t bh = t / (T + Np);
-    float ks[8], vs[8];
-    if (r < T) {
-      unpack8(k[(bh * L + r) * cpt + c], ks);
-      unpack8(v[(bh * L + r) * cpt + c], vs);
-      kp[i] = pack8_f16(ks);
-      vp[i] = pack8_f16(vs);
-      continue;
-    }
-    int np = (int)(r - T);
-    int by = np / Wp, bx = np % Wp;
-    const uint4* kb = k + (bh * L + T) * cpt + c;
-    const uint4* vb = v + (bh * L + T) * cpt + c;
-    if (mode == AREA_POOL_CENTER) {
-      int64_t n = (int64_t)(by * f + f / 2) * Gw + (bx * f + f / 2);
-      unpack8(kb[n * cpt], ks);
-      unpack8(vb[n * cpt], vs);
-    } else {
+                                                   uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
+                                                   int Gh, int Gw, int f, int mode, int T, InvFreq fr) {
+  constexpr int CPT = D / 8;
+  const int Wp = Gw / f, Hp = Gh / f;
+  const int64_t per_bh = ((int64_t)T + (int64_t)Hp * Wp) * CPT;  // output chunks per (batch, head)
+  const int64_t L = T + (int64_t)Gh * Gw;                          // input rows per (batch, head)
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < per_bh;
+         j += (int64_t)gridDim.x * blockDim.x) {
+      const int c = (int)(j & (CPT - 1));
+      const int64_t r = j / CPT;
+      const int64_t i = bh * per_bh + j;
+      float ks[8], vs[8];
+      if (r < T) {
+        unpack8(k[(bh * L + r) * CPT + c], ks);
+        unpack8(v[(bh * L + r) * CPT + c], vs);
+        kp[i] = pack8_f16(ks);
+        vp[i] = pack8_f16(vs);
+        continue;
+      }
+      const int np = (int)(r - T);
+      const int by = np / Wp, bx = np - (np / Wp) * Wp;
+      const uint4* kb = k + (bh * L + T) * CPT + c;
+      const uint4* vb = v + (bh * L + T) * CPT + c;
+      if (mode == AREA_POOL_CENTER) {
+        int64_t n = (int64_t)(by * f + f / 2) * Gw + (bx * f + f / 2);
+        unpack8(kb[n * CPT], ks);
+        unpack8(vb[n * CPT], vs);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ks[j] = vs[j] = 0.0f;
-      for (int dy = 0; dy < f; ++dy) {
-        int64_t row = (int64_t)(by * f + dy) * Gw + bx * f;
-        for (int dx = 0; dx < f; ++dx) {
-          float a[8], b[8];
-          unpack8(kb[(row + dx) * cpt], a);
-          unpack8(vb[(row + dx) * cpt], b);
+        for (int jj = 0; jj < 8; ++jj) ks[jj] = vs[jj] = 0.0f;
+        for (int dy = 0; dy < f; ++dy) {
+          int64_t row = (int64_t)(by * f + dy) * Gw + bx * f;
+          for (int dx = 0; dx < f; ++dx) {
+            float a[8], b[8];
+            unpack8(kb[(row + dx) * CPT], a);
+            unpack8(vb[(row + dx) * CPT], b);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            ks[j] += a[j];
-            vs[j] += b[j];
+            for (int jj = 0; jj < 8; ++jj) {
+              ks[jj] += a[jj];
+              vs[jj] += b[jj];
+            }
           }
         }
-      }
-      float inv = (float)(f * f);
+        float inv = (float)(f * f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ks[j] = ks[j] / inv;
-        vs[j] = vs[j] / inv;
+        for (int jj = 0; jj < 8; ++jj) {
+          ks[jj] = ks[jj] / inv;
+          vs[jj] = vs[jj] / inv;
+        }
       }
+      rope_apply(ks, rope_cs(c, D, (float)by, (float)bx, fr));
+      kp[i] = pack8_f16(ks);
+      vp[i] = pack8_f16(vs);
     }
-    rope8(ks, c, D, (float)by, (float)bx, fr);
-    kp[i] = pack8_f16(ks);
-    vp[i] = pack8_f16(vs);
   }
 }
 
@@ -230,24 +256,40 @@ int check_launch(const char* what) {
 
 }  // namespace
 
+// 2-D launch for the per-(batch, head) kernels: x covers `per_bh` items of
+// one (batch, head) in 256-thread blocks, y the (batch, head) pairs.
+static dim3 grid_2d(int64_t per_bh, int64_t BH) {
+  int64_t gx = (per_bh + 255) / 256;
+  int64_t gy = BH;
+  gx = std::max<int64_t>(1, std::min<int64_t>(gx, 1 << 16));
+  gy = std::max<int64_t>(1, std::min<int64_t>(gy, 65535));
+  return dim3((unsigned)gx, (unsigned)gy);
+}
+
 int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
                 int T, int Gh, int Gw, int D, float theta, float div, stream_t s) {
   const int L = T + Gh * Gw;
-  int64_t total = BH * (int64_t)L * (D / 8);
   InvFreq f = make_inv_freq(D, theta);
-  hipLaunchKernelGGL(prep_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)s, (const uint4*)q,
-                     (const uint4*)k, (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, total, L, T, Gw,
-                     D, div, f);
+  const dim3 grid = grid_2d((int64_t)L * (D / 8), BH);
+  if (D == 128)
+    hipLaunchKernelGGL((prep_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)q, (const uint4*)k,
+                       (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, BH, L, T, Gw, div, f);
+  else
+    hipLaunchKernelGGL((prep_kernel<64>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)q, (const uint4*)k,
+                       (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, BH, L, T, Gw, div, f);
   return check_launch("prep_kernel");
 }
 
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw, int D,
                 int f, int mode, float theta, stream_t s) {
-  int64_t total = BH * ((int64_t)T + (int64_t)(Gh / f) * (Gw / f)) * (D / 8);
   InvFreq fr = make_inv_freq(D, theta);
-  hipLaunchKernelGGL(pool_kernel, dim3(grid_for(total)), dim3(256), 0, (hipStream_t)s,
-                     (const uint4*)k, (const uint4*)v, (uint4*)kp, (uint4*)vp, total, Gh, Gw, D, f,
-                     mode, T, fr);
+  const dim3 grid = grid_2d(((int64_t)T + (int64_t)(Gh / f) * (Gw / f)) * (D / 8), BH);
+  if (D == 128)
+    hipLaunchKernelGGL((pool_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
+                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, fr);
+  else
+    hipLaunchKernelGGL((pool_kernel<64>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
+                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, fr);
   return check_launch("pool_kernel");
 }
 
