@@ -324,6 +324,12 @@ def main():
         "window_kernel_tflops": win_tflops,
         "pool_gbs": pool_bytes / (agg["pool"] * 1e-3) / 1e9 if agg["pool"] > 0 else 0.0,
         "dwt_gbs": dwt_bytes / (agg["dwt"] * 1e-3) / 1e9 if agg["dwt"] > 0 else 0.0,
+        # per-phase speedups: full attention over one Phase I step (pool + coarse) and over one
+        # Phase II step (DWT map + plan + windowed attention), averaged over each phase's steps
+        "speedup_phase1": (full_ms * n_coarse / (agg["pool"] + agg["coarse_call"])
+                           if agg["pool"] + agg["coarse_call"] > 0 else None),
+        "speedup_phase2": (full_ms * n_win / (agg["dwt"] + agg["plan"] + agg["window_call"])
+                           if agg["dwt"] + agg["plan"] + agg["window_call"] > 0 else None),
         "per_step_ms": [round(sum(per_step[s]) / len(per_step[s]), 3) for s in sorted(per_step)],
         "schedule_tflop": (coarse_fl + win_fl) / 1e12,
     }
