@@ -309,6 +309,9 @@ def main():
                      for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
     dwt_bytes = n_win * (wl.C * N * 4 + (N // 4) * 8)
 
+    # ---- the matrix-core rate this GPU sustains (register-only MFMA stream), for context
+    mfma_measured = A.area_measure_mfma_peak()
+
     # ---- CPU oracle baseline on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -367,6 +370,12 @@ def main():
             "avg_launch_ms": round(agg["window_kernel"] / max(n_win, 1), 4),
         },
         "cpu_baseline": cpu,
+        "measured_peak": {
+            "what": "register-only v_mfma_f32_32x32x16_f16 stream on this GPU (area_measure_mfma_peak)",
+            "mfma_tflops": round(mfma_measured, 1),
+            "window_kernel_frac": round(win_tflops / mfma_measured, 4) if mfma_measured > 0 else None,
+            "full_attn_frac": round(full_tflops / mfma_measured, 4) if mfma_measured > 0 else None,
+        },
     }
     print(json.dumps(result), flush=True)
 

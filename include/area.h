@@ -188,6 +188,19 @@ size_t area_plan_words(const area_problem* p);
  * Thread-local; returns AREA_OK, or AREA_E_INVALID if exactly one is NULL. */
 int area_set_attn_events(void* ev_begin, void* ev_end);
 
+/* Measurement hook (not needed for computing): the fp16/bf16 matrix-core
+ * rate the current device sustains.  Launches a register-only stream of
+ * v_mfma_f32_32x32x16_f16 (eight 256-thread work-groups per CU, four
+ * independent accumulators per wave, no memory traffic) twice on `stream`,
+ * times the second launch with HIP events and returns TFLOP/s in *tflops,
+ * the ceiling that the attention kernels are compared with next to the
+ * published peak (the shader clock under load sits below nominal).
+ * Synchronises `stream`.  `sink` is a caller-owned device buffer of at least
+ * 4 bytes; the kernel's only store to it sits under a condition that cannot
+ * hold, so it is never written.  Returns AREA_OK, AREA_E_INVALID if a pointer
+ * is NULL, or AREA_E_HIP. */
+int area_measure_mfma_peak(void* sink, double* tflops, void* stream);
+
 /* Human-readable text for a status, and the thread's last error detail. */
 const char* area_strerror(int status);
 const char* area_last_error(void);

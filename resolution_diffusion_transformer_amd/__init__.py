@@ -118,6 +118,7 @@ _SIGS = {
     "area_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int]),
     "area_plan_words": (ctypes.c_size_t, [ctypes.c_void_p]),
     "area_set_attn_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "area_measure_mfma_peak": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
     "area_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "area_last_error": (ctypes.c_char_p, []),
     "area_pool_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
@@ -216,6 +217,16 @@ def area_set_attn_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
 
 
 # ----------------------------------------------------------- device calls --
+
+def area_measure_mfma_peak() -> float:
+    """Sustained fp16/bf16 matrix-core rate of the current device in TFLOP/s
+    (register-only MFMA stream; synchronises the current stream)."""
+    torch = _torch()
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = ctypes.c_double(0.0)
+    _check(lib().area_measure_mfma_peak(ctypes.c_void_p(sink.data_ptr()), ctypes.byref(out), _stream()))
+    return float(out.value)
+
 
 def _torch():
     import torch

@@ -513,6 +513,11 @@ int area_set_attn_events(void* ev_begin, void* ev_end) {
   return AREA_OK;
 }
 
+int area_measure_mfma_peak(void* sink, double* tflops, void* stream) {
+  if (!sink || !tflops) return fail(AREA_E_INVALID, "NULL sink or result pointer");
+  return measure_mfma_peak(sink, tflops, stream);
+}
+
 int area_pool_kv(const area_problem* p, int f, const void* k, const void* v, void* kp, void* vp,
                  void* stream) {
   int rc = validate(p);

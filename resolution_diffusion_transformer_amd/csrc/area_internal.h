@@ -76,6 +76,9 @@ struct AttnEvents {
 };
 AttnEvents& attn_events();
 
+// Register-only MFMA stream timed on `stream` (area_measure_mfma_peak).
+int measure_mfma_peak(void* sink, double* tflops, void* stream);
+
 // ---------------------------------------------------------- launchers ----
 // Each returns AREA_OK or AREA_E_HIP (with the error text set).  Arguments
 // have been validated by the caller.

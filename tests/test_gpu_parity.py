@@ -251,3 +251,10 @@ def test_window_2048_every_step(flux2048):
             o_ref = O.window_attention(qh[:, h:h + 1], kh[:, h:h + 1], vh[:, h:h + 1], ref,
                                        br_ref[:, h:h + 1], wl.Gh, wl.Gw, wl.rope_theta, rows=rows)
             assert_close(oh[:, h:h + 1, rows], o_ref, f"window 2048 step {t} head {h}")
+
+
+def test_measured_mfma_peak_is_plausible():
+    # register-only MFMA stream: below the published 2.5 PF (the clock under load is below
+    # nominal), and far above what any memory-bound kernel could reach
+    t = A.area_measure_mfma_peak()
+    assert 500.0 < t < 2600.0, t
