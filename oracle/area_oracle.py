@@ -24,7 +24,7 @@ Sources (page titles, sections):
             repository layout.
 
 Where the pages leave a step open, the reading taken is marked READING and
-named (R1...R20); each is one small function here.
+named (R1...R22); each is one small function here.
 
 Text tokens (READING R20, [summary] Phase I: text tokens are never pooled,
 so each of the N image queries attends to T + N/f^2 keys): with T > 0 the
@@ -141,7 +141,8 @@ def text_attention(q, k, v, Gh: int, Gw: int, theta: float, T: int) -> np.ndarra
 # Phase I: pooled keys/values and cross-scale coarse attention
 # ----------------------------------------------------------------------------
 
-POOL_MEAN, POOL_CENTER = 0, 1
+POOL_MEAN, POOL_CENTER, POOL_MEDOID, POOL_RANDOM = 0, 1, 2, 3
+POOL_STREAM = 0x504F4F4C  # "POOL": random pooling draws from its own SplitMix64 stream
 
 
 def pool_tokens(t: np.ndarray, Gh: int, Gw: int, f: int, mode: int) -> np.ndarray:
@@ -166,17 +167,92 @@ def pool_tokens(t: np.ndarray, Gh: int, Gw: int, f: int, mode: int) -> np.ndarra
     return p.reshape(lead + ((Gh // f) * (Gw // f), D))
 
 
-def pool_kv(k, v, Gh: int, Gw: int, f: int, mode: int, theta: float, T: int = 0):
+def block_tokens(Gw: int, f: int, by: int, bx: int) -> np.ndarray:
+    """Token indices of block (by, bx), row-major inside the block: in-block
+    offset o is token (by*f + o // f, bx*f + o % f)."""
+    o = np.arange(f * f)
+    return (by * f + o // f) * Gw + (bx * f + o % f)
+
+
+def pool_random_offset(seed: int, f: int, block: int) -> int:
+    """READING R21 of random pooling ([blog] "Cómo entra en tu pipeline": the
+    tunable pooling takes subsample / mean / medoid / random, and the seed
+    controls random pooling; [summary] Main Findings: random pooling in the
+    representative ablation).  One in-block offset per (pooling factor,
+    block), the same for every batch, head, K and V:
+    splitmix64(seed ^ POOL_STREAM, 1 + f * 2^32 + block) mod f^2."""
+    return int(splitmix64(seed ^ POOL_STREAM, 1 + f * (1 << 32) + block) % (f * f))
+
+
+def medoid_offset(kb: np.ndarray) -> int:
+    """READING R22 of medoid pooling (same passages as R21): the medoid of a
+    block is its token whose key has the smallest sum of Euclidean distances
+    to the block's keys (un-rotated), ties to the smaller in-block offset.
+    kb is [f*f, D] in in-block order.  float64 in a fixed order, so a second
+    implementation that follows it decides the same way: per pair the
+    squared differences summed over d ascending, the square root, then the
+    sum over the other token i ascending."""
+    kb = np.asarray(kb, np.float64)
+    n, D = kb.shape
+    best, best_j = None, 0
+    for j in range(n):
+        total = 0.0
+        for i in range(n):
+            s = 0.0
+            diff = kb[i] - kb[j]
+            for d in range(D):
+                s = s + diff[d] * diff[d]
+            total = total + math.sqrt(s)
+        if best is None or total < best:
+            best, best_j = total, j
+    return best_j
+
+
+def pool_offsets(k: np.ndarray, Gh: int, Gw: int, f: int, mode: int, seed: int = 0) -> np.ndarray:
+    """In-block offset of the representative token of every block, for the
+    single-token modes (center, medoid, random): [..., (Gh/f)*(Gw/f)] int.
+    Medoid decides per leading index (batch, head) on that head's keys."""
+    k = np.asarray(k, np.float64)
+    lead = k.shape[:-2]
+    nb = (Gh // f) * (Gw // f)
+    out = np.zeros(lead + (nb,), np.int64)
+    for b in range(nb):
+        by, bx = divmod(b, Gw // f)
+        if mode == POOL_CENTER:
+            out[..., b] = (f // 2) * f + f // 2
+        elif mode == POOL_RANDOM:
+            out[..., b] = pool_random_offset(seed, f, b)
+        elif mode == POOL_MEDOID:
+            toks = block_tokens(Gw, f, by, bx)
+            for idx in np.ndindex(*lead):
+                out[idx + (b,)] = medoid_offset(k[idx][toks])
+        else:
+            raise ValueError("pool mode")
+    return out
+
+
+def pool_kv(k, v, Gh: int, Gw: int, f: int, mode: int, theta: float, T: int = 0, seed: int = 0):
     """Pooled keys (rotated at integer coarse positions (by, bx)) and pooled
     values (never rotated).  Keys are pooled before rotation so that the
     pooled key carries the coarse-grid position ([summary] Phase I: pooled
-    keys sit on the (W/f) x (H/f) grid).  With T text tokens, the T text keys
-    (position (0, 0): unrotated) and values come first, unpooled ([summary]
-    Phase I: text tokens are never pooled)."""
+    keys sit on the (W/f) x (H/f) grid).  Mean averages the block; the other
+    modes take one token of the block, the same token for K and V (its
+    offset from pool_offsets; medoid chooses it on the keys).  With T text
+    tokens, the T text keys (position (0, 0): unrotated) and values come
+    first, unpooled ([summary] Phase I: text tokens are never pooled)."""
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    kp = pool_tokens(k[..., T:, :], Gh, Gw, f, mode)
-    vp = pool_tokens(v[..., T:, :], Gh, Gw, f, mode)
+    ki, vi = k[..., T:, :], v[..., T:, :]
+    if mode == POOL_MEAN:
+        kp = pool_tokens(ki, Gh, Gw, f, mode)
+        vp = pool_tokens(vi, Gh, Gw, f, mode)
+    else:
+        off = pool_offsets(ki, Gh, Gw, f, mode, seed)
+        nb = off.shape[-1]
+        bys, bxs = np.divmod(np.arange(nb), Gw // f)
+        tok = (bys * f + off // f) * Gw + (bxs * f + off % f)  # [..., nb] token per block
+        kp = np.take_along_axis(ki, tok[..., None], axis=-2)
+        vp = np.take_along_axis(vi, tok[..., None], axis=-2)
     by, bx = grid_positions(Gh // f, Gw // f)
     kp = apply_rope_2d(kp, by, bx, theta)
     return np.concatenate([k[..., :T, :], kp], axis=-2), np.concatenate([v[..., :T, :], vp], axis=-2)

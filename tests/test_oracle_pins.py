@@ -162,6 +162,87 @@ def test_pool_f1_is_identity():
         np.testing.assert_array_equal(O.pool_tokens(t, 4, 5, 1, mode), t)
 
 
+def test_pool_kv_center_takes_the_strided_slice_token():
+    # pool_kv picks single tokens through in-block offsets; for center that must be the
+    # strided-slice token of pool_tokens, rotated at the coarse position
+    g = rng(15)
+    Gh, Gw, f, D = 12, 18, 3, 8
+    k, v = g.standard_normal((2, 1, 2, Gh * Gw, D))
+    kp, vp = O.pool_kv(k, v, Gh, Gw, f, O.POOL_CENTER, 1e4)
+    by, bx = O.grid_positions(Gh // f, Gw // f)
+    np.testing.assert_array_equal(vp, O.pool_tokens(v, Gh, Gw, f, O.POOL_CENTER))
+    np.testing.assert_array_equal(kp, O.apply_rope_2d(O.pool_tokens(k, Gh, Gw, f, O.POOL_CENTER), by, bx, 1e4))
+
+
+def test_medoid_of_collinear_keys_is_the_median():
+    # keys t_i * u on a line: the sum of |t_i - t_j| is smallest at the median of t
+    g = rng(16)
+    for f in (3, 5):
+        t = g.permutation(f * f).astype(np.float64) * 0.37 - 2.0
+        u = g.standard_normal(6)
+        kb = t[:, None] * u[None, :]
+        assert O.medoid_offset(kb) == int(np.argsort(t)[(f * f) // 2])
+
+
+def test_medoid_matches_library_distances():
+    # independent of the oracle's loops: scipy's pairwise Euclidean distances, summed per
+    # candidate, argmin (random keys make ties impossible in practice)
+    from scipy.spatial.distance import cdist
+    g = rng(17)
+    for f in (2, 3, 4, 6):
+        kb = g.standard_normal((f * f, 16))
+        assert O.medoid_offset(kb) == int(np.argmin(cdist(kb, kb).sum(axis=0)))
+
+
+def test_medoid_invariances_and_majority():
+    g = rng(18)
+    kb = g.standard_normal((9, 5))
+    j = O.medoid_offset(kb)
+    assert O.medoid_offset(kb + g.standard_normal(5)) == j          # translation
+    assert O.medoid_offset(3.0 * kb) == j                           # scale
+    maj = np.repeat(kb[4:5], 9, axis=0)
+    maj[[0, 8]] = kb[[0, 8]] * 5.0                                 # 7 of 9 keys identical
+    assert O.medoid_offset(maj) == 1                                # smallest offset holding it
+    assert O.medoid_offset(kb[:1]) == 0                             # one token
+
+
+def test_random_pool_offsets():
+    f, nb = 4, 6000
+    offs = np.array([O.pool_random_offset(7, f, b) for b in range(nb)])
+    assert offs.min() >= 0 and offs.max() < f * f
+    counts = np.bincount(offs, minlength=f * f)
+    # uniform over the f^2 offsets: every count within 5 sigma of nb / f^2
+    mu = nb / (f * f)
+    assert np.all(np.abs(counts - mu) < 5 * np.sqrt(mu))
+    assert [O.pool_random_offset(7, f, b) for b in range(20)] == list(offs[:20])
+    assert [O.pool_random_offset(8, f, b) for b in range(20)] != list(offs[:20])
+    assert O.pool_random_offset(7, 1, 3) == 0
+    # the draw is the POOL stream of SplitMix64 at counter 1 + f * 2^32 + block
+    assert O.pool_random_offset(7, f, 5) == O.splitmix64(7 ^ 0x504F4F4C, 1 + f * (1 << 32) + 5) % (f * f)
+
+
+def test_single_token_pooling_shares_the_token_between_k_and_v():
+    # medoid chooses on K; V takes the same token: with V = K the pooled V is the
+    # un-rotated pooled K, and with f = 1 every mode is the identity
+    g = rng(19)
+    Gh, Gw, D = 6, 6, 8
+    k = g.standard_normal((1, 2, Gh * Gw, D))
+    for mode in (O.POOL_MEDOID, O.POOL_RANDOM):
+        off = O.pool_offsets(k, Gh, Gw, 3, mode, seed=3)
+        kp, vp = O.pool_kv(k, k, Gh, Gw, 3, mode, 1e4, seed=3)
+        by, bx = O.grid_positions(2, 2)
+        np.testing.assert_allclose(kp, O.apply_rope_2d(vp, by, bx, 1e4), rtol=0, atol=0)
+        k1, v1 = O.pool_kv(k, k, Gh, Gw, 1, mode, 1e4, seed=3)
+        y, x = O.grid_positions(Gh, Gw)
+        np.testing.assert_array_equal(v1, k)
+    # medoid decides per head: the two heads' offsets come from their own keys
+    off = O.pool_offsets(k, Gh, Gw, 3, O.POOL_MEDOID)
+    for h in range(2):
+        for b in range(4):
+            by, bx = divmod(b, 2)
+            assert off[0, h, b] == O.medoid_offset(k[0, h][O.block_tokens(Gw, 3, by, bx)])
+
+
 def test_coarse_f1_equals_full_attention():
     g = rng(14)
     Gh, Gw, D = 6, 8, 16
