@@ -396,13 +396,16 @@ def main():
 
 def run_ablation(A, wl, base, args):
     """Attention-time ablations of the AReA schedule (quadrant splits off,
-    Halo off, bridge off, fixed smallest window) and the pages' own knob
-    values, each against the same full-attention baseline; prints one JSON
-    line."""
+    Halo off, bridge off, fixed smallest window, the other Phase I pooling
+    modes) and the pages' own knob values, each against the same
+    full-attention baseline; prints one JSON line."""
     import torch
     import workloads as W
     variants = [("as configured", {}), ("no quadrant splits", {"split_num": 0}), ("no halo", {"halo": 0}),
                 ("no bridge", {"bridge_k": 0}), (f"fixed w={wl.w_min}", {"w_start": wl.w_min}),
+                ("pooling: block centre", {"pool_mode": A.POOL_CENTER}),
+                ("pooling: medoid", {"pool_mode": A.POOL_MEDOID}),
+                ("pooling: random", {"pool_mode": A.POOL_RANDOM}),
                 ("pages' knobs (w_start rule, seeded Halo <= 8, bridge (w/2)^2)", dict(W.PAGES_KNOBS))]
     rows = []
     full_ms = None

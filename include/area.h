@@ -64,6 +64,8 @@ extern "C" {
 /* ---- enums ------------------------------------------------------------- */
 #define AREA_POOL_MEAN   0     /* average of the f x f block                    */
 #define AREA_POOL_CENTER 1     /* token at offset (f/2, f/2) of the block       */
+#define AREA_POOL_MEDOID 2     /* block token with the least summed key distance */
+#define AREA_POOL_RANDOM 3     /* seeded random token of the block              */
 
 #define AREA_PHASE_FULL   0    /* canvas at or below native: keep full attention */
 #define AREA_PHASE_COARSE 1    /* Phase I step                                   */
@@ -114,7 +116,7 @@ typedef struct area_problem {
   int32_t p1_steps;           /* Phase I (coarse) steps                          */
   int32_t f0;                 /* first pooling factor; 0 = derive from native    */
   int32_t f_min;              /* pooling floor (2)                               */
-  int32_t pool_mode;          /* AREA_POOL_MEAN | AREA_POOL_CENTER               */
+  int32_t pool_mode;          /* AREA_POOL_MEAN | _CENTER | _MEDOID | _RANDOM    */
   int32_t p2_steps;           /* Phase II (window) steps                         */
   int32_t w_start, w_min;     /* window side at the first / last Phase II step;  */
                               /* w_start 0 = derive (largest even side whose     */
@@ -213,8 +215,16 @@ const char* area_last_error(void);
  * mantissa bits finer than bf16).  Block (by, bx) sits at index
  * by*(Gw/f)+bx.
  * kp = RoPE(pool(k)) at integer coarse position (by, bx); vp = pool(v).
- * pool = mean of the block's f*f tokens (fp32 sum, one rounding) or the
- * block-centre token per p->pool_mode.  f must divide Gh and Gw. */
+ * pool per p->pool_mode (blog "Cómo entra en tu pipeline": the pooling
+ * tunable takes subsample, mean, medoid or random): the mean of the block's
+ * f*f tokens (fp32 sum, one rounding), or one token of the block, the same
+ * token for K and V: the block centre (offset (f/2, f/2)); the medoid (the
+ * token whose un-rotated key has the smallest sum of Euclidean distances to
+ * the block's keys, float64, per pair the squared differences summed over
+ * d ascending, then the square roots summed over the other token ascending;
+ * ties to the smaller row-major offset; per batch and head); or a random
+ * token, offset SplitMix64(seed ^ 0x504F4F4C, 1 + f*2^32 + block) mod f^2,
+ * the same for every batch and head.  f must divide Gh and Gw. */
 int area_pool_kv(const area_problem* p, int f, const void* k, const void* v,
                  void* kp, void* vp, void* stream);
 

@@ -194,18 +194,15 @@ def medoid_offset(kb: np.ndarray) -> int:
     sum over the other token i ascending."""
     kb = np.asarray(kb, np.float64)
     n, D = kb.shape
-    best, best_j = None, 0
-    for j in range(n):
-        total = 0.0
-        for i in range(n):
-            s = 0.0
-            diff = kb[i] - kb[j]
-            for d in range(D):
-                s = s + diff[d] * diff[d]
-            total = total + math.sqrt(s)
-        if best is None or total < best:
-            best, best_j = total, j
-    return best_j
+    diff = kb[:, None, :] - kb[None, :, :]          # [i, j, d]
+    s = np.zeros((n, n))
+    for d in range(D):                              # d ascending, one rounding per step
+        s = s + diff[:, :, d] * diff[:, :, d]
+    dist = np.sqrt(s)
+    total = np.zeros(n)
+    for i in range(n):                              # other token i ascending
+        total = total + dist[i, :]
+    return int(np.argmin(total))                    # first minimum: the smaller offset
 
 
 def pool_offsets(k: np.ndarray, Gh: int, Gw: int, f: int, mode: int, seed: int = 0) -> np.ndarray:

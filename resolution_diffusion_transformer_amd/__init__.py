@@ -20,11 +20,11 @@ __all__ = [
     "area_plan_words", "area_pool_kv", "area_coarse_attn", "area_dwt_detail",
     "area_window_plan", "area_window_attn", "area_full_attn", "area_text_attn", "area_attn_step",
     "area_set_attn_events",
-    "POOL_MEAN", "POOL_CENTER", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
+    "POOL_MEAN", "POOL_CENTER", "POOL_MEDOID", "POOL_RANDOM", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
     "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "OP_STEP", "PLAN_HEADER", "PLAN_REC",
 ]
 
-POOL_MEAN, POOL_CENTER = 0, 1
+POOL_MEAN, POOL_CENTER, POOL_MEDOID, POOL_RANDOM = 0, 1, 2, 3
 PHASE_FULL, PHASE_COARSE, PHASE_WINDOW = 0, 1, 2
 OP_FULL, OP_COARSE, OP_PLAN, OP_WINDOW, OP_STEP = 0, 1, 2, 3, 4
 PLAN_HEADER, PLAN_REC = 16, 10

@@ -234,7 +234,7 @@ static int validate(const area_problem* pp) {
   if (!(p.rope_theta > 0.0f) || !std::isfinite(p.rope_theta))
     return fail(AREA_E_INVALID, "rope_theta must be positive and finite");
   if (p.p1_steps < 0 || p.p2_steps < 0) return fail(AREA_E_INVALID, "step counts must be >= 0");
-  if (p.pool_mode != AREA_POOL_MEAN && p.pool_mode != AREA_POOL_CENTER)
+  if (p.pool_mode < AREA_POOL_MEAN || p.pool_mode > AREA_POOL_RANDOM)
     return fail(AREA_E_INVALID, pstr("pool_mode", p.pool_mode));
   if (p.f_min < 1 || p.f0 < 0) return fail(AREA_E_INVALID, "f_min must be >= 1 and f0 >= 0");
   if (p.halo < 0 || p.bridge_k < 0 || p.halo_max < 0)
@@ -524,7 +524,8 @@ int area_pool_kv(const area_problem* p, int f, const void* k, const void* v, voi
   if (rc) return rc;
   if (!k || !v || !kp || !vp) return fail(AREA_E_INVALID, "NULL tensor");
   if (f < 1 || p->Gh % f || p->Gw % f) return fail(AREA_E_SHAPE, pstr("f must divide both grid sides, f", f));
-  return launch_pool(k, v, kp, vp, BH_of(*p), p->T, p->Gh, p->Gw, p->D, f, p->pool_mode, p->rope_theta, stream);
+  return launch_pool(k, v, kp, vp, BH_of(*p), p->T, p->Gh, p->Gw, p->D, f, p->pool_mode, p->seed, p->rope_theta,
+                     stream);
 }
 
 int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp, const void* vp,

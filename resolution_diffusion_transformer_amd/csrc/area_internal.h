@@ -90,7 +90,7 @@ typedef void* stream_t;
 int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
                 int T, int Gh, int Gw, int D, float theta, float div, stream_t s);
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw,
-                int D, int f, int mode, float theta, stream_t s);
+                int D, int f, int mode, unsigned long long seed, float theta, stream_t s);
 int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int Gh, int Gw,
                stream_t s);
 

@@ -64,6 +64,25 @@ __device__ inline uint4 pack8(const float* x) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// k-th output of the SplitMix64 generator (Steele, Lea and Flood, OOPSLA
+// 2014) started from `seed`: golden-gamma increment, variant-13 finalizer.
+__device__ inline unsigned long long splitmix64(unsigned long long seed, unsigned long long k) {
+  unsigned long long z = seed + k * 0x9E3779B97F4A7C15ULL;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// Random pooling (READING R21): one in-block offset per (pooling factor,
+// block), drawn on its own SplitMix64 stream ("POOL"), shared by every
+// batch, head, K and V.
+constexpr unsigned long long kPoolStream = 0x504F4F4CULL;
+
+__device__ inline int random_pool_offset(unsigned long long seed, int f, long long block) {
+  const unsigned long long key = 1ULL + ((unsigned long long)f << 32) + (unsigned long long)block;
+  return (int)(splitmix64(seed ^ kPoolStream, key) % (unsigned long long)(f * f));
+}
+
 // Rotation of the 8 channels [8c, 8c+8) of a token at grid position
 // (py, px): channels below D/2 follow the row, the others the column; pair
 // (2k, 2k+1) of an axis half turns by pos * inv_freq[k].  rope_cs computes
@@ -143,15 +162,18 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, 
 // The first T output rows are the text keys and values, copied unpooled and
 // unrotated (text sits at position (0, 0)).  For a pooled row, mean mode
 // sums the block's f*f tokens in fp32 (block rows in order, then columns)
-// and divides by f*f; centre mode takes token (f/2, f/2) of the block.  Keys
-// are then rotated at the coarse position (by, bx); values are not rotated.
+// and divides by f*f; centre mode takes token (f/2, f/2) of the block and
+// random mode the token at its seeded offset (medoid mode has a kernel of its
+// own below).  Keys are then rotated at the coarse position (by, bx); values
+// are not rotated.
 // One rounding at the end, to fp16 (the attention MFMA operand type).
 // Grid as for prep_kernel: x over the (output row, chunk) pairs of one
 // (batch, head), y over (batch, head).
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                    uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
-                                                   int Gh, int Gw, int f, int mode, int T, InvFreq fr) {
+                                                   int Gh, int Gw, int f, int mode, int T, unsigned long long seed,
+                                                   InvFreq fr) {
   constexpr int CPT = D / 8;
   const int Wp = Gw / f, Hp = Gh / f;
   const int64_t per_bh = ((int64_t)T + (int64_t)Hp * Wp) * CPT;  // output chunks per (batch, head)
@@ -174,8 +196,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, 
       const int by = np / Wp, bx = np - (np / Wp) * Wp;
       const uint4* kb = k + (bh * L + T) * CPT + c;
       const uint4* vb = v + (bh * L + T) * CPT + c;
-      if (mode == AREA_POOL_CENTER) {
-        int64_t n = (int64_t)(by * f + f / 2) * Gw + (bx * f + f / 2);
+      if (mode == AREA_POOL_CENTER || mode == AREA_POOL_RANDOM) {
+        const int o = mode == AREA_POOL_CENTER ? (f / 2) * f + f / 2 : random_pool_offset(seed, f, np);
+        int64_t n = (int64_t)(by * f + o / f) * Gw + (bx * f + o % f);
         unpack8(kb[n * CPT], ks);
         unpack8(vb[n * CPT], vs);
       } else {
@@ -204,6 +227,92 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, 
       rope_apply(ks, rope_cs(c, D, (float)by, (float)bx, fr));
       kp[i] = pack8_f16(ks);
       vp[i] = pack8_f16(vs);
+    }
+  }
+}
+
+// Medoid pooling (READING R22), one wave per output row of one (batch,
+// head): rows below T copy the text token; pooled row T + b finds the medoid
+// of block b -- the token whose un-rotated key has the smallest sum of
+// Euclidean distances to the block's keys -- in float64 with every operation
+// in the written order (no contraction): per pair, the squared differences
+// summed over d ascending, the square root, then the sum over the other
+// token ascending; ties go to the smaller row-major offset.  Lanes take the
+// candidates in turn and a wave reduction picks the winner; then the row is
+// written like the other modes: K rotated at the coarse position (by, bx),
+// V unrotated, both fp16.
+template <int D>
+__global__ __launch_bounds__(64) void pool_medoid_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                         uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
+                                                         int Gh, int Gw, int f, int T, InvFreq fr) {
+#pragma clang fp contract(off)
+  constexpr int CPT = D / 8;
+  const int lane = threadIdx.x;
+  const int Wp = Gw / f;
+  const int64_t rows_out = (int64_t)T + (int64_t)(Gh / f) * Wp;
+  const int64_t L = T + (int64_t)Gh * Gw;
+  const int64_t r = blockIdx.x;
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const uint4* kb = k + bh * L * CPT;
+    const uint4* vb = v + bh * L * CPT;
+    int64_t src;
+    int by = 0, bx = 0;
+    if (r < T) {
+      src = r;
+    } else {
+      const int b = (int)(r - T);
+      by = b / Wp;
+      bx = b - by * Wp;
+      const int n = f * f;
+      auto tok = [&](int o) -> int64_t { return T + (int64_t)(by * f + o / f) * Gw + (bx * f + o % f); };
+      double best = 0.0;
+      int best_j = n;  // none yet
+      for (int j = lane; j < n; j += 64) {
+        const uint4* kj = kb + tok(j) * CPT;
+        double total = 0.0;
+        for (int i = 0; i < n; ++i) {
+          const uint4* ki = kb + tok(i) * CPT;
+          double s = 0.0;
+          for (int c = 0; c < CPT; ++c) {
+            float a[8], bv[8];
+            unpack8(ki[c], a);
+            unpack8(kj[c], bv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const double diff = (double)a[e] - (double)bv[e];
+              s = s + diff * diff;
+            }
+          }
+          total = total + __builtin_sqrt(s);
+        }
+        if (best_j == n || total < best) {
+          best = total;
+          best_j = j;
+        }
+      }
+      // wave argmin: the smaller total wins, equal totals go to the smaller offset
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const double ob = __shfl_xor(best, m);
+        const int oj = __shfl_xor(best_j, m);
+        const bool take = oj < n && (best_j == n || ob < best || (ob == best && oj < best_j));
+        best = take ? ob : best;
+        best_j = take ? oj : best_j;
+      }
+      src = tok(best_j);
+    }
+    uint4* ko = kp + (bh * rows_out + r) * CPT;
+    uint4* vo = vp + (bh * rows_out + r) * CPT;
+    for (int c = lane; c < 2 * CPT; c += 64) {
+      float x[8];
+      if (c < CPT) {
+        unpack8(kb[src * CPT + c], x);
+        if (r >= T) rope_apply(x, rope_cs(c, D, (float)by, (float)bx, fr));
+        ko[c] = pack8_f16(x);
+      } else {
+        unpack8(vb[src * CPT + (c - CPT)], x);
+        vo[c - CPT] = pack8_f16(x);
+      }
     }
   }
 }
@@ -281,15 +390,27 @@ int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko,
 }
 
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw, int D,
-                int f, int mode, float theta, stream_t s) {
+                int f, int mode, unsigned long long seed, float theta, stream_t s) {
   InvFreq fr = make_inv_freq(D, theta);
-  const dim3 grid = grid_2d(((int64_t)T + (int64_t)(Gh / f) * (Gw / f)) * (D / 8), BH);
+  const int64_t rows_out = (int64_t)T + (int64_t)(Gh / f) * (Gw / f);
+  if (mode == AREA_POOL_MEDOID) {
+    if (rows_out > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "too many pooled rows for the medoid grid");
+    const dim3 grid((unsigned)rows_out, (unsigned)std::min<int64_t>(BH, 65535));
+    if (D == 128)
+      hipLaunchKernelGGL((pool_medoid_kernel<128>), grid, dim3(64), 0, (hipStream_t)s, (const uint4*)k,
+                         (const uint4*)v, (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, T, fr);
+    else
+      hipLaunchKernelGGL((pool_medoid_kernel<64>), grid, dim3(64), 0, (hipStream_t)s, (const uint4*)k,
+                         (const uint4*)v, (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, T, fr);
+    return check_launch("pool_medoid_kernel");
+  }
+  const dim3 grid = grid_2d(rows_out * (D / 8), BH);
   if (D == 128)
     hipLaunchKernelGGL((pool_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
-                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, fr);
+                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
   else
     hipLaunchKernelGGL((pool_kernel<64>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
-                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, fr);
+                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
   return check_launch("pool_kernel");
 }
 

@@ -72,15 +72,19 @@ def test_full_attention_tiny(tiny):
     assert_close(to_host(out), ref, "full tiny")
 
 
-@pytest.mark.parametrize("mode", [A.POOL_MEAN, A.POOL_CENTER])
+@pytest.mark.parametrize("mode", [A.POOL_MEAN, A.POOL_CENTER, A.POOL_MEDOID, A.POOL_RANDOM])
 @pytest.mark.parametrize("f", [1, 2, 4])
 def test_pool_and_coarse_tiny(tiny, mode, f):
     wl, q, k, v, qh, kh, vh = tiny
-    p = A.problem_for(wl, pool_mode=mode)
+    p = A.problem_for(wl, pool_mode=mode, seed=11)
     kp, vp = A.area_pool_kv(p, f, k, v)
     out = A.area_coarse_attn(p, f, q, kp, vp)
     torch.cuda.synchronize()
-    kp_ref, vp_ref = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, mode, wl.rope_theta)
+    kp_ref, vp_ref = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, mode, wl.rope_theta, seed=11)
+    if mode != A.POOL_MEAN:
+        # one token per block, the same as the oracle's: the pooled V rows are the chosen
+        # tokens' values rounded once to fp16, bit for bit
+        np.testing.assert_array_equal(vp.cpu().numpy(), vp_ref.astype(np.float16), f"vp tokens f={f} mode={mode}")
     # pooled tensors: one bf16 rounding of the fp32 result
     assert_close(to_host(kp), kp_ref, f"kp f={f} mode={mode}", max_abs=2e-2, mean_abs=2e-3)
     assert_close(to_host(vp), vp_ref, f"vp f={f} mode={mode}", max_abs=2e-2, mean_abs=2e-3)
@@ -258,3 +262,18 @@ def test_measured_mfma_peak_is_plausible():
     # nominal), and far above what any memory-bound kernel could reach
     t = A.area_measure_mfma_peak()
     assert 500.0 < t < 2600.0, t
+
+
+@pytest.mark.parametrize("mode", [A.POOL_MEDOID, A.POOL_RANDOM])
+def test_single_token_pooling_2048(flux2048, mode):
+    # 128 x 128 grid, D = 128, f = 2 and 4: the chosen token of every block of two heads
+    # equals the oracle's (medoid decides in float64 in the same order as the oracle)
+    wl, q, k, v, qh, kh, vh = flux2048
+    p = A.problem_for(wl, pool_mode=mode, seed=5)
+    for f in (2, 4):
+        kp, vp = A.area_pool_kv(p, f, k, v)
+        torch.cuda.synchronize()
+        got = vp.cpu().numpy()
+        for h in (0, 13):
+            _, vp_ref = O.pool_kv(kh[:, h:h + 1], vh[:, h:h + 1], wl.Gh, wl.Gw, f, mode, wl.rope_theta, seed=5)
+            np.testing.assert_array_equal(got[:, h:h + 1], vp_ref.astype(np.float16), f"f={f} head {h}")
