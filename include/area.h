@@ -148,7 +148,7 @@ typedef struct area_step {
 
 /* ---- host-only calls (no GPU needed) ------------------------------------ */
 
-/* Checks a problem: sizes positive, D in {64, 128}, T == 0, both grid sides
+/* Checks a problem: sizes positive, D in {64, 128}, 0 <= T <= 2^20, both grid sides
  * even, a common factor >= max(2, f_min) when the canvas exceeds native
  * (README canvas rules), w_min <= w_start, window sides even and >= 2,
  * bridge cells fit the grid, split_den > 0.  Returns AREA_OK or an error. */
@@ -162,6 +162,17 @@ int area_validate(const area_problem* p);
  * (ai.info summary, Methodology, Phase II).  At or below native every step
  * is AREA_PHASE_FULL. */
 int area_step_info(const area_problem* p, int step, area_step* out);
+
+/* Phase I step count from a sampler's noise schedule (ai.info summary,
+ * Scheduling the switch; README sigma* paragraph: the switch is a noise
+ * level sigma*, 0.86 .. 0.96 for the tuned models, not a step count).
+ * sigmas[0 .. n_steps-1] are the noise levels of the denoising steps in
+ * order; *p1_steps receives the number of leading steps with
+ * sigmas[t] > sigma_star (the first step at or below sigma_star starts
+ * Phase II, later steps stay there).  Use it as area_problem.p1_steps and
+ * n_steps - *p1_steps as p2_steps.  Host only.  Returns AREA_OK, or
+ * AREA_E_INVALID for NULL pointers, n_steps < 0 or a NaN sigma_star. */
+int area_phase1_steps_for_sigma(const double* sigmas, int n_steps, double sigma_star, int* p1_steps);
 
 /* First pooling factor (f0 from the problem, or derived from the native
  * grid when p->f0 == 0).  Returns the factor or a negative status. */

@@ -24,7 +24,7 @@ Sources (page titles, sections):
             repository layout.
 
 Where the pages leave a step open, the reading taken is marked READING and
-named (R1...R22); each is one small function here.
+named (R1...R23); each is one small function here.
 
 Text tokens (READING R20, [summary] Phase I: text tokens are never pooled,
 so each of the N image queries attends to T + N/f^2 keys): with T > 0 the
@@ -760,9 +760,23 @@ def canvas_check(Gh: int, Gw: int, native_h: int, native_w: int, f_min: int = 2)
 def step_phases(p1_steps: int, p2_steps: int) -> List[int]:
     """READING R16: a fixed count of coarse steps, then the window steps
     ([summary] Scheduling the switch: 8 steps for FLUX.1, 20 for
-    Qwen-Image; the sigma threshold itself needs a sampler and is not
-    modelled)."""
+    Qwen-Image).  phase1_steps_for_sigma turns a sampler's noise levels and
+    a threshold sigma* into that count."""
     return [PHASE_COARSE] * p1_steps + [PHASE_WINDOW] * p2_steps
+
+
+def phase1_steps_for_sigma(sigmas: Sequence[float], sigma_star: float) -> int:
+    """READING R23 ([summary] Scheduling the switch and [readme] sigma*
+    paragraph: the switch from Phase I to Phase II is a noise level sigma*,
+    not a step count): Phase I runs the leading steps whose noise level is
+    above sigma*; the first step at or below sigma* starts Phase II, and
+    every later step stays there."""
+    n = 0
+    for s in sigmas:
+        if not s > sigma_star:
+            break
+        n += 1
+    return n
 
 
 # ----------------------------------------------------------------------------

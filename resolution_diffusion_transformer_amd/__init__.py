@@ -119,6 +119,8 @@ _SIGS = {
     "area_plan_words": (ctypes.c_size_t, [ctypes.c_void_p]),
     "area_set_attn_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     "area_measure_mfma_peak": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
+    "area_phase1_steps_for_sigma": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_double,
+                                                   ctypes.POINTER(ctypes.c_int)]),
     "area_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "area_last_error": (ctypes.c_char_p, []),
     "area_pool_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5),
@@ -217,6 +219,16 @@ def area_set_attn_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
 
 
 # ----------------------------------------------------------- device calls --
+
+def area_phase1_steps_for_sigma(sigmas, sigma_star: float) -> int:
+    """Number of leading denoising steps whose noise level is above sigma_star
+    (Phase I); host only."""
+    vals = [float(x) for x in sigmas]
+    arr = (ctypes.c_double * max(len(vals), 1))(*vals)
+    out = ctypes.c_int(0)
+    _check(lib().area_phase1_steps_for_sigma(arr, len(vals), float(sigma_star), ctypes.byref(out)))
+    return int(out.value)
+
 
 def area_measure_mfma_peak() -> float:
     """Sustained fp16/bf16 matrix-core rate of the current device in TFLOP/s

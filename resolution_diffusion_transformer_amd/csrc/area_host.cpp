@@ -513,6 +513,16 @@ int area_set_attn_events(void* ev_begin, void* ev_end) {
   return AREA_OK;
 }
 
+int area_phase1_steps_for_sigma(const double* sigmas, int n_steps, double sigma_star, int* p1_steps) {
+  if (!p1_steps || (n_steps > 0 && !sigmas)) return fail(AREA_E_INVALID, "NULL sigmas or result pointer");
+  if (n_steps < 0) return fail(AREA_E_INVALID, pstr("n_steps", n_steps));
+  if (sigma_star != sigma_star) return fail(AREA_E_INVALID, "sigma_star is NaN");
+  int n = 0;
+  while (n < n_steps && sigmas[n] > sigma_star) ++n;
+  *p1_steps = n;
+  return AREA_OK;
+}
+
 int area_measure_mfma_peak(void* sink, double* tflops, void* stream) {
   if (!sink || !tflops) return fail(AREA_E_INVALID, "NULL sink or result pointer");
   return measure_mfma_peak(sink, tflops, stream);

@@ -246,3 +246,20 @@ def test_pages_knob_validation():
     with pytest.raises(A.AreaError) as e:
         A.area_validate(prob("tiny-32", bridge_rho_num=4, bridge_rho_den=1))
     assert e.value.status == -2
+
+
+def test_phase1_steps_for_sigma_matches_oracle():
+    g = np.random.default_rng(21)
+    for _ in range(50):
+        n = int(g.integers(0, 40))
+        sig = np.sort(g.random(n))[::-1]
+        s_star = float(g.random())
+        assert A.area_phase1_steps_for_sigma(sig, s_star) == O.phase1_steps_for_sigma(list(sig), s_star)
+    L = A.lib()
+    out = ctypes.c_int(-7)
+    arr = (ctypes.c_double * 2)(0.9, 0.5)
+    assert L.area_phase1_steps_for_sigma(arr, 2, 0.7, ctypes.byref(out)) == 0 and out.value == 1
+    assert L.area_phase1_steps_for_sigma(None, 2, 0.7, ctypes.byref(out)) == -1
+    assert L.area_phase1_steps_for_sigma(arr, -1, 0.7, ctypes.byref(out)) == -1
+    assert L.area_phase1_steps_for_sigma(arr, 2, float("nan"), ctypes.byref(out)) == -1
+    assert L.area_phase1_steps_for_sigma(arr, 2, 0.7, None) == -1

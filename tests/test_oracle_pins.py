@@ -779,3 +779,18 @@ def test_text_brute_force_tiny():
             w = min(y - win.qy0 + 1, win.qh - (y - win.qy0)) * min(x - win.qx0 + 1, win.qw - (x - win.qx0))
             acc, wsum = acc + w * o, wsum + w
         np.testing.assert_allclose(wo[b, h, n], acc / wsum, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------ sigma switch --
+
+def test_phase1_steps_for_sigma():
+    # linear schedule sigma_t = 1 - t / n: the steps above sigma* are t < n (1 - sigma*)
+    n = 28
+    sig = [1.0 - t / n for t in range(n)]
+    for s_star in (0.86, 0.9, 0.93, 0.96):
+        assert O.phase1_steps_for_sigma(sig, s_star) == math.ceil(n * (1.0 - s_star) - 1e-12)
+    assert O.phase1_steps_for_sigma(sig, 1.5) == 0            # sigma* above every level
+    assert O.phase1_steps_for_sigma(sig, -1.0) == n           # below every level
+    assert O.phase1_steps_for_sigma(sig, sig[3]) == 3         # a level equal to sigma* is Phase II
+    assert O.phase1_steps_for_sigma([0.99, 0.8, 0.97], 0.9) == 1   # no switching back
+    assert O.phase1_steps_for_sigma([], 0.9) == 0
