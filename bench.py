@@ -463,8 +463,10 @@ def measured_traffic(workload):
 
 
 def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
-    """The oracle on head 0 of two steps (first coarse step, last window
-    step), scaled by algorithmic work to the whole schedule and all heads."""
+    """The oracle on head 0 of three steps (the first coarse step, the middle
+    and the last window step), scaled by algorithmic work to the whole
+    schedule and all heads: each phase's steps take the sampled steps'
+    seconds per FLOP of that phase."""
     import numpy as np
     import resolution_diffusion_transformer_amd as A
     from oracle import area_oracle as O
@@ -473,35 +475,41 @@ def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    log("[bench] cpu baseline: oracle on head 0 of the first coarse and the last window step")
+    log("[bench] cpu baseline: oracle on head 0 of the first coarse, the middle and the last window step")
     qh = q[:, :1].float().cpu().numpy().astype(np.float64)
     kh = k[:, :1].float().cpu().numpy().astype(np.float64)
     vh = v[:, :1].float().cpu().numpy().astype(np.float64)
     latn = lat.cpu().numpy()
-    s_c = next(s for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE)
-    s_w = max(s for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW)
-    f = sched[s_c]["f"]
-    t0 = time.perf_counter()
-    kp, vp = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, O.POOL_MEAN, wl.rope_theta)
-    O.coarse_attention(qh, kp, vp, wl.Gh, wl.Gw, f, wl.rope_theta)
-    t_c = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    t = s_w - wl.p1_steps
-    Eq = O.energy_fixed(O.detail_energy(latn))
-    plan = O.window_plan(wl.Gh, wl.Gw, sched[s_w]["w"], wl.halo, wl.seed, t, Eq)
-    br = O.bridge_select(kh[0, 0], wl.bridge_k, wl.Gh, wl.Gw)[None, None]
-    O.window_attention(qh, kh, vh, plan, br, wl.Gh, wl.Gw, wl.rope_theta)
-    t_w = time.perf_counter() - t0
+    coarse = [s for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE]
+    window = [s for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW]
+    c_samples = coarse[:1]
+    w_samples = sorted({window[len(window) // 2], window[-1]}) if window else []
+    t_c = 0.0
+    for s_c in c_samples:
+        f = sched[s_c]["f"]
+        t0 = time.perf_counter()
+        kp, vp = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, O.POOL_MEAN, wl.rope_theta)
+        O.coarse_attention(qh, kp, vp, wl.Gh, wl.Gw, f, wl.rope_theta)
+        t_c += time.perf_counter() - t0
+    t_w = 0.0
+    Eq = O.energy_fixed(O.detail_energy(latn)) if w_samples else None
+    for s_w in w_samples:
+        t0 = time.perf_counter()
+        t = s_w - wl.p1_steps
+        plan = O.window_plan(wl.Gh, wl.Gw, sched[s_w]["w"], wl.halo, wl.seed, t, Eq)
+        br = O.bridge_select(kh[0, 0], wl.bridge_k, wl.Gh, wl.Gw)[None, None]
+        O.window_attention(qh, kh, vh, plan, br, wl.Gh, wl.Gw, wl.rope_theta)
+        t_w += time.perf_counter() - t0
     H = wl.H * wl.B
-    # the sample is one head; flops[] ratios move it along the schedule, H scales it to all heads
-    coarse_total = H * sum(t_c * flops[s] / flops[s_c] for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE)
-    win_total = H * sum(t_w * flops[s] / flops[s_w] for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW)
+    # the samples are one head; their seconds per FLOP move them along each phase, H scales to all heads
+    coarse_total = (H * t_c * sum(flops[s] for s in coarse) / sum(flops[s] for s in c_samples)) if c_samples else 0.0
+    win_total = (H * t_w * sum(flops[s] for s in window) / sum(flops[s] for s in w_samples)) if w_samples else 0.0
     ms_per_step = (coarse_total + win_total) * 1e3 / n_steps
     return {"value": round(ms_per_step, 1), "unit": "ms/step", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle on head 0 of {H}: coarse step {s_c} (f={f}, all {wl.N} queries) "
-                       f"took {t_c:.2f} s, window step {s_w} (w={sched[s_w]['w']}, plan + bridge + "
-                       f"attention, all queries) took {t_w:.2f} s; scaled by algorithmic FLOPs to all "
-                       f"{n_steps} steps and {H} heads"),
+            "sample": (f"float64 NumPy oracle on head 0 of {H}: coarse step {c_samples} (all {wl.N} queries) took "
+                       f"{t_c:.2f} s; window steps {w_samples} (w={[sched[s]['w'] for s in w_samples]}, plan + "
+                       f"bridge + attention, all queries) took {t_w:.2f} s; each phase scaled by its samples' "
+                       f"seconds per algorithmic FLOP to all {n_steps} steps and {H} heads"),
             "sample_seconds": round(t_c + t_w, 2)}
 
 
