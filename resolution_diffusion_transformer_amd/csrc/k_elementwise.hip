@@ -118,29 +118,55 @@ __device__ inline void rope_apply(float* x, const Rot4& r) {
 // written as IEEE fp16 (the MFMA operand type of the attention kernels;
 // bf16 -> fp16 is exact in fp16's normal range and the rotated values keep
 // three more mantissa bits than bf16 would).  k / v may be null to skip them.
-// Grid: x over the (row, chunk) pairs of one (batch, head), y over (batch,
-// head), both grid-strided; D is a template parameter so the chunk split is
-// a shift.
+// A block takes kPrepSeg consecutive rows of the sequence for kPrepHeads
+// (batch, head) pairs: it first tabulates the rows' (cos, sin) for every
+// frequency of both axis halves (the same sincosf of the same angle as a
+// per-element rotation, so the result is identical), then streams the
+// heads' chunks through the table.
+constexpr int kPrepSeg = 64;
+constexpr int kPrepHeads = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
                                                    const uint4* __restrict__ v, uint4* __restrict__ qo,
                                                    uint4* __restrict__ ko, uint4* __restrict__ vo, int64_t BH,
                                                    int L, int T, int Gw, float div, InvFreq f) {
-  constexpr int CPT = D / 8;
-  const int64_t per_bh = (int64_t)L * CPT;
-  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < per_bh;
-         j += (int64_t)gridDim.x * blockDim.x) {
-      const int c = (int)(j & (CPT - 1));
-      const int n = (int)(j / CPT) - T;
-      float py = 0.0f, px = 0.0f;
-      if (n >= 0) {
-        const int yy = n / Gw;
-        py = (float)yy / div;
-        px = (float)(n - yy * Gw) / div;
+  constexpr int CPT = D / 8;  // 16-byte chunks per row
+  constexpr int NF = D / 4;   // frequencies per axis half
+  __shared__ float2 tab[kPrepSeg][2 * NF];  // [row][axis * NF + k] = (cos, sin)
+  const int64_t row0 = (int64_t)blockIdx.x * kPrepSeg;
+  for (int e = threadIdx.x; e < kPrepSeg * 2 * NF; e += blockDim.x) {
+    const int t = e / (2 * NF), a = e - t * (2 * NF);
+    const int64_t row = row0 + t;
+    float pos = 0.0f;
+    if (row < L && row >= T) {
+      const int n = (int)(row - T);
+      const int yy = n / Gw;
+      pos = a < NF ? (float)yy / div : (float)(n - yy * Gw) / div;
+    }
+    float sn, co;
+    sincosf(pos * f.v[a < NF ? a : a - NF], &sn, &co);
+    tab[t][a] = make_float2(co, sn);
+  }
+  __syncthreads();
+  const int rows = (int)min((int64_t)kPrepSeg, (int64_t)L - row0);
+  for (int64_t bh0 = (int64_t)blockIdx.y * kPrepHeads; bh0 < BH; bh0 += (int64_t)gridDim.y * kPrepHeads) {
+    for (int e = threadIdx.x; e < kPrepHeads * rows * CPT; e += blockDim.x) {
+      const int hh = e / (rows * CPT), rem = e - hh * (rows * CPT);
+      const int t = rem / CPT, c = rem - t * CPT;
+      const int64_t bh = bh0 + hh;
+      if (bh >= BH) continue;
+      // chunk c: channels 8c .. 8c+7, pairs k0 .. k0+3 of its axis half
+      const int d0 = 8 * c;
+      const int base = (d0 < D / 2 ? 0 : NF) + (d0 % (D / 2)) / 2;
+      Rot4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 cs = tab[t][base + j];
+        r.co[j] = cs.x;
+        r.sn[j] = cs.y;
       }
-      const Rot4 r = rope_cs(c, D, py, px, f);
-      const int64_t i = bh * per_bh + j;
+      const int64_t i = (bh * L + row0 + t) * CPT + c;
       float x[8];
       unpack8(q[i], x);
       rope_apply(x, r);
@@ -167,8 +193,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, 
 // own below).  Keys are then rotated at the coarse position (by, bx); values
 // are not rotated.
 // One rounding at the end, to fp16 (the attention MFMA operand type).
-// Grid as for prep_kernel: x over the (output row, chunk) pairs of one
-// (batch, head), y over (batch, head).
+// Grid: x over the (output row, chunk) pairs of one (batch, head), y over
+// (batch, head), both grid-strided.
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                    uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
@@ -379,7 +405,9 @@ int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko,
                 int T, int Gh, int Gw, int D, float theta, float div, stream_t s) {
   const int L = T + Gh * Gw;
   InvFreq f = make_inv_freq(D, theta);
-  const dim3 grid = grid_2d((int64_t)L * (D / 8), BH);
+  const int64_t segs = ((int64_t)L + kPrepSeg - 1) / kPrepSeg;
+  if (segs > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "sequence too long for the prep grid");
+  const dim3 grid((unsigned)segs, (unsigned)std::min<int64_t>((BH + kPrepHeads - 1) / kPrepHeads, 65535));
   if (D == 128)
     hipLaunchKernelGGL((prep_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)q, (const uint4*)k,
                        (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, BH, L, T, Gw, div, f);
