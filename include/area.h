@@ -196,7 +196,8 @@ size_t area_plan_words(const area_problem* p);
  * (area_full_attn, area_coarse_attn, area_window_attn) records the HIP event
  * `ev_begin` just before the kernel and `ev_end` just after it, on the
  * call's stream, so a profiler-free caller can time the MFMA kernel alone
- * (without the operand preparation and blend kernels around it).  Events
+ * (without the key preparation, gather and blend kernels around it; the
+ * queries' RoPE and fp16 conversion run inside the kernel).  Events
  * are hipEvent_t handles owned by the caller; pass NULL, NULL to clear.
  * Thread-local; returns AREA_OK, or AREA_E_INVALID if exactly one is NULL. */
 int area_set_attn_events(void* ev_begin, void* ev_end);

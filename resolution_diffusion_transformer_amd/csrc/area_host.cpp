@@ -299,7 +299,7 @@ static WindowMax window_max(const area_problem& p) {
 
 // Regions of the windowed-attention workspace, in order.
 struct WindowLayout {
-  size_t q, k, slots, items, kg, vg, blist, bcount, total;
+  size_t rope, slots, items, kg, vg, blist, bcount, total;
 };
 
 static WindowLayout window_layout(const area_problem& p) {
@@ -312,9 +312,7 @@ static WindowLayout window_layout(const area_problem& p) {
     off += align_up(bytes);
     return at;
   };
-  // rotated Q and K first, in the places the text pass of a step reads them
-  l.q = take(tok_bytes(p));
-  l.k = take(tok_bytes(p));
+  l.rope = take(rope_table_bytes(p.Gh, p.Gw, p.D));
   l.slots = take((size_t)m.q_total * BH * p.D * 4);
   l.items = take(window_items_ws_bytes(m.max_windows, m.max_items, m.n_base, m.max_gtiles));
   l.kg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
@@ -383,10 +381,11 @@ static size_t workspace_bytes(const area_problem& p, int op) {
   switch (op) {
     case AREA_OP_STEP:
       return step_layout(p).total;
-    case AREA_OP_FULL:
-      return 2 * align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D));
-    case AREA_OP_COARSE:
-      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D));
+    case AREA_OP_FULL:  // rotated K, V^T tiles, (cos, sin) table
+      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D)) +
+             align_up(rope_table_bytes(p.Gh, p.Gw, p.D));
+    case AREA_OP_COARSE:  // V^T tiles of the pooled values, (cos, sin) table
+      return align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D)) + align_up(rope_table_bytes(p.Gh, p.Gw, p.D));
     case AREA_OP_PLAN: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
       WindowMax m = window_max(p);
@@ -549,14 +548,14 @@ int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp
   int64_t BH = BH_of(*p);
   int N = (int)N_of(*p);
   int M = N / (f * f);
-  char* qr = (char*)ws;
-  char* vt = qr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, nullptr, nullptr, qr, nullptr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, (float)f,
-                   stream);
+  char* vt = (char*)ws;
+  char* tab = vt + align_up(vt_bytes(BH, (int)L_of(*p), p->D));
+  // queries turn at coarse-grid positions (row / f, column / f), as the keys
+  rc = launch_rope_table(tab, p->Gh, p->Gw, p->D, p->rope_theta, (float)f, stream);
   if (rc) return rc;
   rc = launch_vt(vp, vt, BH, p->T + M, p->D, false, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kp, vt, out, BH, N, p->T, p->T + N, p->T + M, p->D, stream);
+  return launch_dense_attn(q, tab, p->T, p->Gh, p->Gw, kp, vt, out, BH, N, p->T, p->T + N, p->T + M, p->D, stream);
 }
 
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out,
@@ -567,34 +566,40 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
   rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
   if (rc) return rc;
   int64_t BH = BH_of(*p);
-  int N = (int)N_of(*p);
-  char* qr = (char*)ws;
-  char* kr = qr + align_up(tok_bytes(*p));
+  const int L = (int)L_of(*p);
+  char* kr = (char*)ws;
   char* vt = kr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  char* tab = vt + align_up(vt_bytes(BH, L, p->D));
+  rc = launch_rope_table(tab, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
   if (rc) return rc;
-  const int L = p->T + N;
+  rc = launch_prep(k, kr, tab, BH, p->T, p->Gh, p->Gw, p->D, stream);
+  if (rc) return rc;
   rc = launch_vt(v, vt, BH, L, p->D, true, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kr, vt, out, BH, L, 0, L, L, p->D, stream);
+  return launch_dense_attn(q, tab, p->T, p->Gh, p->Gw, kr, vt, out, BH, L, 0, L, L, p->D, stream);
 }
 
 }  // extern "C"
 
 namespace area {
 
-// The text queries against every key, from rotated fp16 Q and K already at
-// the start of a full-attention-shaped workspace (Q rows at 0, K rows at the
-// next aligned offset): V^T after them, then dense attention over T queries.
-static int text_pass(const area_problem& p, char* ws, const void* v, void* out, void* stream) {
+// The T text queries against every key (text and image), in a workspace of
+// the full-attention layout: rotated fp16 K, V^T tiles, (cos, sin) table.
+// Text queries sit at position (0, 0), so they are not turned.
+static int text_pass(const area_problem& p, char* ws, const void* q, const void* k, const void* v, void* out,
+                     void* stream) {
   const int64_t BH = BH_of(p);
   const int L = (int)L_of(p);
-  char* qr = ws;
-  char* kr = qr + align_up(tok_bytes(p));
+  char* kr = ws;
   char* vt = kr + align_up(tok_bytes(p));
-  int rc = launch_vt(v, vt, BH, L, p.D, true, stream);
+  char* tab = vt + align_up(vt_bytes(BH, L, p.D));
+  int rc = launch_rope_table(tab, p.Gh, p.Gw, p.D, p.rope_theta, 1.0f, stream);
   if (rc) return rc;
-  return launch_dense_attn(qr, kr, vt, out, BH, p.T, 0, L, L, p.D, stream);
+  rc = launch_prep(k, kr, tab, BH, p.T, p.Gh, p.Gw, p.D, stream);
+  if (rc) return rc;
+  rc = launch_vt(v, vt, BH, L, p.D, true, stream);
+  if (rc) return rc;
+  return launch_dense_attn(q, tab, p.T, p.Gh, p.Gw, kr, vt, out, BH, p.T, 0, L, L, p.D, stream);
 }
 
 }  // namespace area
@@ -609,12 +614,7 @@ int area_text_attn(const area_problem* p, const void* q, const void* k, const vo
   if (p->T == 0) return AREA_OK;
   rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
   if (rc) return rc;
-  char* qr = (char*)ws;
-  char* kr = qr + align_up(tok_bytes(*p));
-  rc = launch_prep(q, k, nullptr, qr, kr, nullptr, BH_of(*p), p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
-                   stream);
-  if (rc) return rc;
-  return text_pass(*p, qr, v, out, stream);
+  return text_pass(*p, (char*)ws, q, k, v, out, stream);
 }
 
 int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
@@ -709,10 +709,9 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   w.vg = base + l.vg;
   w.blist = (int*)(base + l.blist);
   w.bcount = (int*)(base + l.bcount);
-  rc = launch_prep(q, k, nullptr, base + l.q, base + l.k, nullptr, a.BH, p->T, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f,
-                   stream);
+  rc = launch_rope_table(base + l.rope, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
   if (rc) return rc;
-  return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, base + l.q, base + l.k, v, out, w, stream);
+  return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, q, k, v, base + l.rope, out, w, stream);
 }
 
 int area_attn_step(const area_problem* p, int step, int C, const float* latent, const void* q,
@@ -754,9 +753,7 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       rc = area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
                             ws_bytes - l.window_ws, stream);
       if (rc || p->T == 0) return rc;
-      // the windowed pass left rotated fp16 Q and K (text rows included) at
-      // the start of its workspace, where the text pass reads them
-      return text_pass(*p, base + l.window_ws, v, out, stream);
+      return text_pass(*p, base + l.window_ws, q, k, v, out, stream);
     }
   }
 }

@@ -84,11 +84,17 @@ int measure_mfma_peak(void* sink, double* tflops, void* stream);
 // have been validated by the caller.
 typedef void* stream_t;
 
-// fp16 attention operands: qo = RoPE(q), ko = RoPE(k) at grid positions
-// (row / div, column / div), vo = v; k/ko and v/vo may be null.
-// Sequences are T text tokens (position (0, 0)) then the Gh x Gw image grid.
-int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
-                int T, int Gh, int Gw, int D, float theta, float div, stream_t s);
+// fp16 keys for dense attention: xo = RoPE(x) at grid positions through
+// the first table of launch_rope_table (built with div 1).  Sequences are T
+// text tokens (position (0, 0), not rotated) then the Gh x Gw image grid.
+int launch_prep(const void* x, void* xo, const void* tab, int64_t BH, int T, int Gh, int Gw, int D, stream_t s);
+// (cos, sin) tables of every axis position p < P = max(Gh, Gw) and
+// frequency k < D/4 at angle (p / div) * theta^(-4k/D), fp32: first
+// [P][D/4] float2 (the windowed gather turns keys through it), then
+// [D/8][P] float4 of frequency pairs (the attention kernels turn queries
+// through it).
+size_t rope_table_bytes(int Gh, int Gw, int D);
+int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, stream_t s);
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw,
                 int D, int f, int mode, unsigned long long seed, float theta, stream_t s);
 int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int Gh, int Gw,
@@ -116,12 +122,14 @@ size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
 size_t vt_bytes(int64_t BH, int M, int D);
 int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, stream_t s);
 
-// Attention over fp16 operands (rotated q, rotated k rows, V^T tiles), bf16
-// output.
-// Queries are rows q0 .. q0 + Nq - 1 of sequences of q_rows rows (q and out
-// share that layout); keys are the Nk rows of k_rot / vt per (batch, head).
-int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH,
-                      int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
+// Attention of bf16 queries (turned by RoPE through the tables `rope` of
+// launch_rope_table as they are loaded; rows below q_text are text, row
+// q_text + n is image token n of the Gh x Gw grid) over fp16 rotated key
+// rows and V^T tiles, bf16 output.  Queries are rows q0 .. q0 + Nq - 1 of sequences of q_rows rows (q
+// and out share that layout); keys are the Nk rows of k_rot / vt per
+// (batch, head).
+int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int Gw, const void* k_rot,
+                      const void* vt, void* out, int64_t BH, int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
 
 struct WindowAttnArgs {
   int Gh, Gw, D, R;
@@ -142,9 +150,12 @@ struct WindowWs {
   int* blist;      // [max_windows][BH][R] kept bridge tokens
   int* bcount;     // [max_windows][BH]
 };
+// q, k, v: un-rotated bf16 sequences; the gather turns the keys and the
+// attention kernel the queries by RoPE through the tables `rope` of
+// launch_rope_table (div 1).
 int launch_window_attn(const WindowAttnArgs& a, const int32_t* plan, const int32_t* wsum,
-                       const int32_t* bridge_idx, const void* q_rot, const void* k_rot,
-                       const void* v, void* out, const WindowWs& ws, stream_t s);
+                       const int32_t* bridge_idx, const void* q, const void* k, const void* v,
+                       const void* rope, void* out, const WindowWs& ws, stream_t s);
 size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base, int64_t max_gtiles);
 
 }  // namespace area

@@ -7,8 +7,11 @@
 //    contiguous run of fp16 K rows plus fp16 V^T tiles of 64 keys: full and
 //    coarse attention use the prepared tensors directly, windowed attention
 //    first gathers each window's keys (Halo rectangle, then the bridge tokens
-//    outside it, compacted) with a bandwidth-bound kernel, so no index math or
-//    transposition remains in the MFMA loop.
+//    outside it, compacted; turned by RoPE on the way) with a bandwidth-bound
+//    kernel, so no index math or transposition remains in the MFMA loop.
+//  * Queries are read once per work item as bf16 and turned by RoPE through
+//    a (cos, sin) table into fp16 registers, so no rotated copy of Q is
+//    written.
 //  * MFMA v_mfma_f32_32x32x16_f16 with fp32 accumulation for Q K^T and P V.
 //    fp16 operands run at the bf16 rate with three more mantissa bits, so the
 //    bf16 rounding of the output is the only coarse rounding on the path.
@@ -36,6 +39,7 @@
 //    window) land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <string>
@@ -72,6 +76,23 @@ __device__ inline u16 f2bf(float f) {
 __device__ inline u16 bf_to_f16(u16 b) {
   _Float16 h = (_Float16)__uint_as_float(((unsigned)b) << 16);
   return __builtin_bit_cast(u16, h);
+}
+
+// Two-axis RoPE of one 16-byte chunk (8 bf16 channels, 4 rotation pairs)
+// into fp16: c01, c23 hold the chunk's four (cos, sin) pairs, interleaved.
+// Pair (a, b) becomes (a cos - b sin, a sin + b cos), rounded to nearest.
+__device__ inline u32x4 rope8_f16(const u32x4 raw, const float4 c01, const float4 c23) {
+  const float co[4] = {c01.x, c01.z, c23.x, c23.z};
+  const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = __uint_as_float(raw[j] << 16), b = __uint_as_float(raw[j] & 0xFFFF0000u);
+    const _Float16 x0 = (_Float16)(a * co[j] - b * sn[j]);
+    const _Float16 x1 = (_Float16)(a * sn[j] + b * co[j]);
+    r[j] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
+  }
+  return r;
 }
 
 // ------------------------------------------------------------ V^T tiles --
@@ -237,19 +258,25 @@ __global__ __launch_bounds__(256) void bridge_compact_kernel(const int32_t* __re
 // Gathers one 64-key tile of a window's key set: slot s < kh*kw is the Halo
 // rectangle token s (row-major), then the compacted outside bridge tokens,
 // then the T text tokens, then zero rows.  Sequences hold the T text rows
-// first, image token n at row T + n.  K rows are copied (already rotated,
-// fp16); V rows are converted bf16 -> fp16 and written transposed.
+// first, image token n at row T + n.  K rows are turned by RoPE at their
+// token's grid position (text rows at (0, 0), unturned) through the (cos,
+// sin) table `rope` and written as fp16; V rows are converted bf16 -> fp16
+// and written transposed.
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan, const int* __restrict__ gtiles,
                                                      const int* __restrict__ n_items, const int* __restrict__ kv_tile_off,
                                                      const int* __restrict__ list, const int* __restrict__ count,
-                                                     const u16* __restrict__ kr, const u16* __restrict__ v,
-                                                     u16* __restrict__ kg, u16* __restrict__ vg, int64_t cap_tiles,
-                                                     int R, int Tt, int Gw, int N, int64_t BH) {
+                                                     const u16* __restrict__ k, const u16* __restrict__ v,
+                                                     const float* __restrict__ rope, u16* __restrict__ kg,
+                                                     u16* __restrict__ vg, int64_t cap_tiles, int R, int Tt, int Gw,
+                                                     int N, int64_t BH) {
   constexpr int CPR = D / 8;
+  constexpr int HALF = CPR / 2;  // chunks per axis half
+  constexpr int NF = D / 4;      // frequencies per axis half
   constexpr int LS = D + 8;
   __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
   __shared__ int s_tok[BN];
+  __shared__ int s_py[BN], s_px[BN];
   const int g = blockIdx.x;
   const int64_t bh = blockIdx.y;
   if (g >= n_items[1]) return;
@@ -262,18 +289,26 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   if (threadIdx.x < BN) {
     int s = t * BN + threadIdx.x;
     int row = -1;  // sequence row of the slot's token
+    int py = 0, px = 0;  // its grid position (text: (0, 0))
     if (s < nrect) {
       int yy = s / kw;
-      row = Tt + (ky0 + yy) * Gw + kx0 + (s - yy * kw);
+      py = ky0 + yy;
+      px = kx0 + (s - yy * kw);
+      row = Tt + py * Gw + px;
     } else if (s - nrect < cnt) {
-      row = Tt + list[((int64_t)rec * BH + bh) * R + (s - nrect)];
+      const int tok = list[((int64_t)rec * BH + bh) * R + (s - nrect)];
+      py = tok / Gw;
+      px = tok - py * Gw;
+      row = Tt + tok;
     } else if (s - nrect - cnt < Tt) {
       row = s - nrect - cnt;
     }
     s_tok[threadIdx.x] = row;
+    s_py[threadIdx.x] = py;
+    s_px[threadIdx.x] = px;
   }
   __syncthreads();
-  const u16* ksrc = kr + bh * (int64_t)(Tt + N) * D;
+  const u16* ksrc = k + bh * (int64_t)(Tt + N) * D;
   const u16* vsrc = v + bh * (int64_t)(Tt + N) * D;
   u16* kdst = kg + (bh * cap_tiles + T) * (int64_t)BN * D;
   for (int c = threadIdx.x; c < BN * CPR; c += 256) {
@@ -281,7 +316,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
     int tok = s_tok[row];
     u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (tok >= 0) {
-      kv = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)tok * D + col * 8);
+      // chunk col: channels 8 col .. 8 col + 7, rotation pairs 4 (col % HALF) ..
+      // of the row (first half) or column (second half) axis
+      const int pos = col < HALF ? s_py[row] : s_px[row];
+      const float4* cs = reinterpret_cast<const float4*>(rope + 2 * (pos * NF + 4 * (col % HALF)));
+      kv = rope8_f16(*reinterpret_cast<const u32x4*>(ksrc + (int64_t)tok * D + col * 8), cs[0], cs[1]);
       vv = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)tok * D + col * 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -304,7 +343,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 
 // -------------------------------------------------------------- attention --
 struct AttnArgs {
-  const u16* q;        // rotated queries, fp16 [BH][q_rows][D]
+  const u16* q;        // un-rotated queries, bf16 [BH][q_rows][D]
+  const float4* rope;  // [D/8][rope_P] (cos, sin) of frequencies 2i, 2i+1 at axis position p
+  int rope_P;          // positions per frequency pair (max(Gh, Gw))
+  int q_text;          // rows below q_text are text (not rotated); row q_text + n is image token n
   const u16* k;        // fp16 key rows [BH][k_rows][D]
   const u16* vt;       // fp16 V^T tiles [BH][k_tiles][D][64]
   u16* out;            // bf16 [BH][q_rows][D]
@@ -325,7 +367,8 @@ struct AttnArgs {
   const int* kv_tile_off;  // per record: first gathered key tile
   const int* bcount;       // [record][BH] bridge tokens kept
   float* slots;            // [slot][BH][D] fp32 outputs of overlapped tokens
-  int Gw, R, T;         // T text keys end every window's key set
+  int Gw;              // grid width (query positions)
+  int R, T;            // window mode: bridge slots and text keys ending every key set
   int64_t max_items;
 };
 
@@ -673,13 +716,35 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
       qtok[g] = qvalid[g] ? t : 0;
     }
   }
-  f16x8 qf[QG][KD];
+  // MFMA B operand: chunk 2 kd + hi (channels 16 kd + 8 hi ..) of the
+  // lane's query, turned by RoPE at its grid position (chunks of the first
+  // half follow the row, the others the column; text rows sit at (0, 0)).
+  // The raw chunks and their (cos, sin) are loaded here and turned after
+  // the first tile DMAs have been started, so the two latencies overlap.
+  u32x4 qraw[QG][KD];
+  float4 qcs[QG][KD][2];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    const f16x8* qrow = reinterpret_cast<const f16x8*>(qbase + (int64_t)qtok[g] * D);
+    const int64_t row = (int64_t)a.q0 + qtok[g];
+    int py = 0, px = 0;
+    if (row >= a.q_text) {
+      const int img = (int)(row - a.q_text);
+      py = img / a.Gw;
+      px = img - py * a.Gw;
+    }
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(qbase + (int64_t)qtok[g] * D);
 #pragma unroll
-    for (int kd = 0; kd < KD; ++kd) qf[g][kd] = qrow[2 * kd + hi];
+    for (int kd = 0; kd < KD; ++kd) {
+      const int ch = 2 * kd + hi;
+      const int pos = kd < KD / 2 ? py : px;
+      // frequencies 4 (ch % KD) .. + 3: pairs 2 (ch % KD) and 2 (ch % KD) + 1
+      const float4* cs = a.rope + (int64_t)(2 * (ch % KD)) * a.rope_P + pos;
+      qraw[g][kd] = qrow[ch];
+      qcs[g][kd][0] = cs[0];
+      qcs[g][kd][1] = cs[a.rope_P];
+    }
   }
+  f16x8 qf[QG][KD];
 
   const int nt = (nkv + BN - 1) / BN;
   const float c = a.c;
@@ -752,6 +817,12 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   issue_k<D>(ks0, 0, tid, wave_u, nkv, kbase);
   issue_v<D>(vt0, 0, tid, wave_u, vtbase);
   issue_k<D>(ks1, min(1, nt - 1), tid, wave_u, nkv, kbase);
+  __builtin_amdgcn_sched_barrier(0);  // all three DMAs before the rotation's waits
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1]));
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   tile_scores<D, QG>(sa, ks0, n, hi, qf);
@@ -945,10 +1016,14 @@ int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, s
   return check_launch("vt_kernel");
 }
 
-int launch_dense_attn(const void* q_rot, const void* k_rot, const void* vt, void* out, int64_t BH, int Nq, int q0,
-                      int q_rows, int Nk, int D, stream_t s) {
+int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int Gw, const void* k_rot,
+                      const void* vt, void* out, int64_t BH, int Nq, int q0, int q_rows, int Nk, int D, stream_t s) {
   AttnArgs a = {};
-  a.q = (const u16*)q_rot;
+  a.q = (const u16*)q;
+  a.rope_P = std::max(Gh, Gw);
+  a.rope = (const float4*)rope + (size_t)a.rope_P * (D / 8);  // second table
+  a.q_text = q_text;
+  a.Gw = Gw;
   a.k = (const u16*)k_rot;
   a.vt = (const u16*)vt;
   a.out = (u16*)out;
@@ -972,7 +1047,8 @@ size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base, int
 }
 
 int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32_t* wsum, const int32_t* bridge_idx,
-                       const void* q_rot, const void* k_rot, const void* v, void* out, const WindowWs& ws, stream_t s) {
+                       const void* q, const void* k, const void* v, const void* rope, void* out, const WindowWs& ws,
+                       stream_t s) {
   hipStream_t st = (hipStream_t)s;
   int n_base = w.ny * w.nx;
   const int R = bridge_idx ? w.R : 0;
@@ -992,16 +1068,21 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   dim3 gg((unsigned)w.max_gtiles, (unsigned)w.BH);
   if (w.D == 128)
     hipLaunchKernelGGL((gather_kernel<128>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
-                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
-                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N, w.BH);
+                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k,
+                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N,
+                       w.BH);
   else
     hipLaunchKernelGGL((gather_kernel<64>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
-                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k_rot,
-                       (const u16*)v, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N, w.BH);
+                       (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k,
+                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N,
+                       w.BH);
   rc = check_launch("gather_kernel");
   if (rc) return rc;
   AttnArgs a = {};
-  a.q = (const u16*)q_rot;
+  a.q = (const u16*)q;
+  a.rope_P = std::max(w.Gh, w.Gw);
+  a.rope = (const float4*)rope + (size_t)a.rope_P * (w.D / 8);  // second table
+  a.q_text = w.T;
   a.k = (const u16*)ws.kg;
   a.vt = (const u16*)ws.vg;
   a.out = (u16*)out;

@@ -111,80 +111,65 @@ __device__ inline void rope_apply(float* x, const Rot4& r) {
   }
 }
 
-// Attention operand preparation, one thread per 8 channels of a token of
-// the joint sequence (T text tokens, then the image grid):
-//   qo = RoPE(q) and ko = RoPE(k) at positions (row / div, col / div) for
-// image tokens and (0, 0) -- no rotation -- for text tokens, vo = v, all
-// written as IEEE fp16 (the MFMA operand type of the attention kernels;
-// bf16 -> fp16 is exact in fp16's normal range and the rotated values keep
-// three more mantissa bits than bf16 would).  k / v may be null to skip them.
-// A block takes kPrepSeg consecutive rows of the sequence for kPrepHeads
-// (batch, head) pairs: it first tabulates the rows' (cos, sin) for every
-// frequency of both axis halves (the same sincosf of the same angle as a
-// per-element rotation, so the result is identical), then streams the
-// heads' chunks through the table.
-constexpr int kPrepSeg = 64;
-constexpr int kPrepHeads = 4;
-
+// Key preparation for dense attention, one thread per 8 channels of a
+// token of the joint sequence (T text tokens, then the image grid):
+// xo = RoPE(x) at the token's grid position (text tokens at (0, 0), not
+// rotated), written as IEEE fp16 (the MFMA operand type of the attention
+// kernels; bf16 -> fp16 is exact in fp16's normal range and the rotated
+// values keep three more mantissa bits than bf16 would).  The (cos, sin)
+// come from the [P][D/4] table of rope_table_kernel.
 template <int D>
-__global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ q, const uint4* __restrict__ k,
-                                                   const uint4* __restrict__ v, uint4* __restrict__ qo,
-                                                   uint4* __restrict__ ko, uint4* __restrict__ vo, int64_t BH,
-                                                   int L, int T, int Gw, float div, InvFreq f) {
-  constexpr int CPT = D / 8;  // 16-byte chunks per row
-  constexpr int NF = D / 4;   // frequencies per axis half
-  __shared__ float2 tab[kPrepSeg][2 * NF];  // [row][axis * NF + k] = (cos, sin)
-  const int64_t row0 = (int64_t)blockIdx.x * kPrepSeg;
-  for (int e = threadIdx.x; e < kPrepSeg * 2 * NF; e += blockDim.x) {
-    const int t = e / (2 * NF), a = e - t * (2 * NF);
-    const int64_t row = row0 + t;
-    float pos = 0.0f;
-    if (row < L && row >= T) {
-      const int n = (int)(row - T);
-      const int yy = n / Gw;
-      pos = a < NF ? (float)yy / div : (float)(n - yy * Gw) / div;
+__global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ x_in, uint4* __restrict__ xo,
+                                                   const float2* __restrict__ tab, int64_t BH, int L, int T,
+                                                   int Gw) {
+  constexpr int CPT = D / 8;     // 16-byte chunks per row
+  constexpr int HALF = CPT / 2;  // chunks per axis half
+  constexpr int NF = D / 4;      // frequencies per axis half
+  const int64_t total = BH * (int64_t)L * CPT;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % CPT);
+    const int row = (int)((i / CPT) % L);
+    int py = 0, px = 0;
+    if (row >= T) {
+      const int n = row - T;
+      py = n / Gw;
+      px = n - py * Gw;
     }
-    float sn, co;
-    sincosf(pos * f.v[a < NF ? a : a - NF], &sn, &co);
-    tab[t][a] = make_float2(co, sn);
-  }
-  __syncthreads();
-  const int rows = (int)min((int64_t)kPrepSeg, (int64_t)L - row0);
-  for (int64_t bh0 = (int64_t)blockIdx.y * kPrepHeads; bh0 < BH; bh0 += (int64_t)gridDim.y * kPrepHeads) {
-    for (int e = threadIdx.x; e < kPrepHeads * rows * CPT; e += blockDim.x) {
-      const int hh = e / (rows * CPT), rem = e - hh * (rows * CPT);
-      const int t = rem / CPT, c = rem - t * CPT;
-      const int64_t bh = bh0 + hh;
-      if (bh >= BH) continue;
-      // chunk c: channels 8c .. 8c+7, pairs k0 .. k0+3 of its axis half
-      const int d0 = 8 * c;
-      const int base = (d0 < D / 2 ? 0 : NF) + (d0 % (D / 2)) / 2;
-      Rot4 r;
+    // chunk c: channels 8c .. 8c+7, pairs 4 (c % HALF) .. + 3 of its axis half
+    const float2* cs = tab + (c < HALF ? py : px) * NF + 4 * (c % HALF);
+    Rot4 r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float2 cs = tab[t][base + j];
-        r.co[j] = cs.x;
-        r.sn[j] = cs.y;
-      }
-      const int64_t i = (bh * L + row0 + t) * CPT + c;
-      float x[8];
-      unpack8(q[i], x);
-      rope_apply(x, r);
-      qo[i] = pack8_f16(x);
-      if (k) {
-        unpack8(k[i], x);
-        rope_apply(x, r);
-        ko[i] = pack8_f16(x);
-      }
-      if (v) {
-        unpack8(v[i], x);
-        vo[i] = pack8_f16(x);
-      }
+    for (int j = 0; j < 4; ++j) {
+      r.co[j] = cs[j].x;
+      r.sn[j] = cs[j].y;
     }
+    float x[8];
+    unpack8(x_in[i], x);
+    rope_apply(x, r);
+    xo[i] = pack8_f16(x);
   }
 }
 
-// Pooled keys/values: one thread per (batch*head, output row, 8 channels).
+// (cos, sin) of every (axis position, frequency) pair the attention kernels
+// rotate by, c_k(p) = sincos((p / div) * inv_freq[k]) for p < P, k < D/4, in
+// two layouts: tab[p][k] (float2; a thread's chunk of one token reads
+// neighbouring frequencies, the windowed gather's access) and
+// tabq[k / 2][p] (float4 = c_k, c_k+1 for even k; lanes holding neighbouring
+// positions read neighbouring entries, the attention kernels' query load).
+// Angles are formed as rope_cs forms those of the pooled keys: the fp32
+// position times the fp32 inverse frequency, then sincosf.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, float2* __restrict__ tabq, int P,
+                                                         int NF, float div, InvFreq f) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= P * NF) return;
+  const int p = e / NF, k = e - p * NF;
+  const float pos = (float)p / div;
+  float sn, co;
+  sincosf(pos * f.v[k], &sn, &co);
+  tab[e] = make_float2(co, sn);
+  tabq[((k >> 1) * P + p) * 2 + (k & 1)] = make_float2(co, sn);
+}
+
 // The first T output rows are the text keys and values, copied unpooled and
 // unrotated (text sits at position (0, 0)).  For a pooled row, mean mode
 // sums the block's f*f tokens in fp32 (block rows in order, then columns)
@@ -401,20 +386,26 @@ static dim3 grid_2d(int64_t per_bh, int64_t BH) {
   return dim3((unsigned)gx, (unsigned)gy);
 }
 
-int launch_prep(const void* q, const void* k, const void* v, void* qo, void* ko, void* vo, int64_t BH,
-                int T, int Gh, int Gw, int D, float theta, float div, stream_t s) {
-  const int L = T + Gh * Gw;
-  InvFreq f = make_inv_freq(D, theta);
-  const int64_t segs = ((int64_t)L + kPrepSeg - 1) / kPrepSeg;
-  if (segs > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "sequence too long for the prep grid");
-  const dim3 grid((unsigned)segs, (unsigned)std::min<int64_t>((BH + kPrepHeads - 1) / kPrepHeads, 65535));
+int launch_prep(const void* x, void* xo, const void* tab, int64_t BH, int T, int Gh, int Gw, int D, stream_t s) {
+  const int64_t total = BH * ((int64_t)T + (int64_t)Gh * Gw) * (D / 8);
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 1 << 20);
   if (D == 128)
-    hipLaunchKernelGGL((prep_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)q, (const uint4*)k,
-                       (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, BH, L, T, Gw, div, f);
+    hipLaunchKernelGGL((prep_kernel<128>), dim3(blocks), dim3(256), 0, (hipStream_t)s, (const uint4*)x, (uint4*)xo,
+                       (const float2*)tab, BH, T + Gh * Gw, T, Gw);
   else
-    hipLaunchKernelGGL((prep_kernel<64>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)q, (const uint4*)k,
-                       (const uint4*)v, (uint4*)qo, (uint4*)ko, (uint4*)vo, BH, L, T, Gw, div, f);
+    hipLaunchKernelGGL((prep_kernel<64>), dim3(blocks), dim3(256), 0, (hipStream_t)s, (const uint4*)x, (uint4*)xo,
+                       (const float2*)tab, BH, T + Gh * Gw, T, Gw);
   return check_launch("prep_kernel");
+}
+
+size_t rope_table_bytes(int Gh, int Gw, int D) { return 2 * (size_t)std::max(Gh, Gw) * (D / 4) * sizeof(float2); }
+
+int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, stream_t s) {
+  const int P = std::max(Gh, Gw), NF = D / 4;
+  float2* t = (float2*)tab;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((int64_t)P * NF)), dim3(256), 0, (hipStream_t)s, t,
+                     t + (size_t)P * NF, P, NF, div, make_inv_freq(D, theta));
+  return check_launch("rope_table_kernel");
 }
 
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw, int D,

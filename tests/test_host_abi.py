@@ -121,7 +121,9 @@ def test_gated_canvas_keeps_full_attention():
     for s in range(12):
         assert A.area_step_info(p, s)["phase"] == A.PHASE_FULL
     assert A.area_workspace_bytes(p, A.OP_WINDOW) == 0
-    assert A.area_workspace_bytes(p, A.OP_FULL) == 3 * p.B * p.H * p.N * p.D * 2
+    # rotated K and V^T tiles (N is a multiple of 64), then the two layouts
+    # of the (cos, sin) table of 64 positions x D/4 frequencies
+    assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * p.B * p.H * p.N * p.D * 2 + 2 * 64 * (p.D // 4) * 8
 
 
 @pytest.mark.parametrize("over,status", [
@@ -174,15 +176,16 @@ def test_device_calls_reject_bad_arguments_before_launch():
 def test_workspace_sizes():
     p = prob("flux-6144")
     tok = p.B * p.H * p.N * p.D * 2
-    assert A.area_workspace_bytes(p, A.OP_FULL) == 3 * tok
-    assert A.area_workspace_bytes(p, A.OP_COARSE) == 2 * tok      # rotated q + V^T tiles
-    # window workspace covers fp16 q, k, gathered k and V^T tiles, and the fp32
+    tab = 2 * max(p.Gh, p.Gw) * (p.D // 4) * 8                 # (cos, sin) tables
+    assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * tok + tab  # rotated k + V^T tiles
+    assert A.area_workspace_bytes(p, A.OP_COARSE) == tok + tab    # V^T tiles
+    # window workspace covers the table, gathered k and V^T tiles, and the fp32
     # outputs of the largest step
     wl = W.get("flux-6144")
     qmax = max(len(O.axis_windows(wl.Gh, w, 0, t, 0)[0]) * len(O.axis_windows(wl.Gw, w, 0, t, 1)[0])
                * min(w, wl.Gh) * min(w, wl.Gw)
                for t, w in enumerate(O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)))
-    assert A.area_workspace_bytes(p, A.OP_WINDOW) >= 2 * tok + qmax * p.B * p.H * p.D * 4
+    assert A.area_workspace_bytes(p, A.OP_WINDOW) >= tab + qmax * p.B * p.H * p.D * 4
     assert A.area_plan_words(p) == A.PLAN_HEADER + A.PLAN_REC * 4 * 36
 
 
