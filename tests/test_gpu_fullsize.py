@@ -189,6 +189,36 @@ def test_batch_two_windowed():
         close(out.float().cpu().numpy(), o_ref, f"batch 2 window step {t} (w={w})")
 
 
+def test_max_windows_per_axis():
+    # w = 2 on a 128 x 128 grid: 64 base windows per axis, the most a step may
+    # have; windows over the smooth half split into 1 x 1 quadrants, giving
+    # 10240 records (2048 whole windows, 8192 quadrants) with one-token queries
+    # and 4 x 4 Halo rectangles plus the bridge.
+    wl, p = small_problem(128, 128, H=2, D=64, w_start=4, w_min=2, halo=1, bridge_k=16)
+    q, k, v = (t.cuda() for t in W.make_qkv(wl, device="cpu", dtype="bf16", seed=7))
+    qh, kh, vh = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+    lat = W.make_latent(wl)
+    _, Eq = A.area_dwt_detail(p, torch.from_numpy(lat).cuda())
+    Eq_ref = O.energy_fixed(O.detail_energy(lat))
+    sizes = O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)
+    assert sizes[-1] == 2 and A.area_step_info(p, wl.p1_steps + 2)["ny"] == 64
+    br_ref = O.bridge_all(kh, wl.bridge_k, wl.Gh, wl.Gw)
+    for t, w in enumerate(sizes):
+        s = wl.p1_steps + t
+        plan, wsum, br = A.area_window_plan(p, s, Eq, k)
+        out = A.area_window_attn(p, s, plan, wsum, br, q, k, v)
+        torch.cuda.synchronize()
+        ref = O.window_plan(wl.Gh, wl.Gw, w, wl.halo, wl.seed, t, Eq_ref)
+        pl = plan.cpu().numpy()
+        nwin = int(pl[0])
+        assert nwin == len(ref.windows), t
+        np.testing.assert_array_equal(pl[16:16 + 10 * nwin].reshape(nwin, 10), ref.records())
+        np.testing.assert_array_equal(wsum.cpu().numpy(), ref.wsum)
+        np.testing.assert_array_equal(br.cpu().numpy(), br_ref)
+        o_ref = O.window_attention(qh, kh, vh, ref, br_ref, wl.Gh, wl.Gw, wl.rope_theta)
+        close(out.float().cpu().numpy(), o_ref, f"64 windows per axis, step {t} (w={w}, {len(ref.windows)} records)")
+
+
 def test_repeated_calls_are_deterministic():
     wl = W.get("tiny-32")
     p = A.problem_for(wl)
