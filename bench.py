@@ -187,6 +187,7 @@ class Schedule:
         agg = {k_: 0.0 for k_ in ("pool", "coarse_call", "coarse_kernel", "dwt", "plan", "window_call",
                                    "window_kernel", "full_call", "full_kernel")}
         per_step = {}
+        parts = {}  # step -> summed component times over the K passes
         for kind, s, e in recs:
             if kind == "coarse":
                 e0, e1, e2, a0, a1 = e
@@ -195,20 +196,44 @@ class Schedule:
                 agg["coarse_call"] += t_call
                 agg["coarse_kernel"] += t_ker
                 per_step.setdefault(s, []).append(t_pool + t_call)
+                c = parts.setdefault(s, {"pool_ms": 0.0, "attn_call_ms": 0.0, "kernel_ms": 0.0})
+                c["pool_ms"] += t_pool
+                c["attn_call_ms"] += t_call
+                c["kernel_ms"] += t_ker
             elif kind == "window":
                 e0, e1, e2, e3, a0, a1 = e
                 t_dwt, t_plan, t_call = e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3)
+                t_ker = ev.elapsed(a0, a1)
                 agg["dwt"] += t_dwt
                 agg["plan"] += t_plan
                 agg["window_call"] += t_call
-                agg["window_kernel"] += ev.elapsed(a0, a1)
+                agg["window_kernel"] += t_ker
                 per_step.setdefault(s, []).append(t_dwt + t_plan + t_call)
+                c = parts.setdefault(s, {"dwt_ms": 0.0, "plan_bridge_ms": 0.0, "attn_call_ms": 0.0, "kernel_ms": 0.0})
+                c["dwt_ms"] += t_dwt
+                c["plan_bridge_ms"] += t_plan
+                c["attn_call_ms"] += t_call
+                c["kernel_ms"] += t_ker
             else:
                 e0, e1, a0, a1 = e
                 agg["full_call"] += e0.elapsed_time(e1)
                 agg["full_kernel"] += ev.elapsed(a0, a1)
         for k_ in agg:
             agg[k_] /= K
+        # one entry per schedule step: its components (ms, averaged over the
+        # passes; attn_call includes the kernel) and the attention kernel's rate
+        self.step_detail = []
+        for s in sorted(parts):
+            st = self.sched[s]
+            d = {"step": s}
+            if st["phase"] == A.PHASE_COARSE:
+                d["phase"], d["f"] = "coarse", st["f"]
+            else:
+                d["phase"], d["w"] = "window", st["w"]
+            for k_, v_ in parts[s].items():
+                d[k_] = round(v_ / K, 3)
+            d["kernel_tflops"] = round(self.flops[s] / (d["kernel_ms"] * 1e-3) / 1e12, 1) if d["kernel_ms"] > 0 else None
+            self.step_detail.append(d)
         area_ms = agg["pool"] + agg["coarse_call"] + agg["dwt"] + agg["plan"] + agg["window_call"]
         return agg, per_step, area_ms
 
@@ -348,6 +373,7 @@ def main():
         "speedup_phase2": (full_ms * n_win / (agg["dwt"] + agg["plan"] + agg["window_call"])
                            if agg["dwt"] + agg["plan"] + agg["window_call"] > 0 else None),
         "per_step_ms": [round(sum(per_step[s]) / len(per_step[s]), 3) for s in sorted(per_step)],
+        "per_step": sc.step_detail,
         "schedule_tflop": (coarse_fl + win_fl) / 1e12,
     }
     result = {

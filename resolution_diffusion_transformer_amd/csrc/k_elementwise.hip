@@ -1,6 +1,6 @@
-// Bandwidth-bound kernels of the AReA path on gfx950: two-axis RoPE
-// rotation, f x f key/value pooling with RoPE at coarse positions, and the
-// Haar detail-energy map.
+// Bandwidth-bound kernels of the AReA path on gfx950: the two-axis RoPE
+// (cos, sin) tables and the fp16 rotation of dense keys, f x f key/value
+// pooling with RoPE at coarse positions, and the Haar detail-energy map.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
