@@ -149,7 +149,8 @@ typedef struct area_step {
 /* ---- host-only calls (no GPU needed) ------------------------------------ */
 
 /* Checks a problem: sizes positive, D in {64, 128}, 0 <= T <= 2^20, both grid sides
- * even, a common factor >= max(2, f_min) when the canvas exceeds native
+ * even and at most 65536 (AREA_E_UNSUPPORTED above), T + Gh*Gw <= 2^30 and
+ * B*H*(T + Gh*Gw)*D <= 2^40, a common factor >= max(2, f_min) when the canvas exceeds native
  * (README canvas rules), w_min <= w_start, window sides even and >= 2,
  * bridge cells fit the grid, split_den > 0.  Returns AREA_OK or an error. */
 int area_validate(const area_problem* p);

@@ -245,6 +245,9 @@ static int validate(const area_problem* pp) {
   long long N = (long long)p.Gh * p.Gw;
   if (N + p.T > (1LL << 30) || (long long)p.B * p.H * (N + p.T) * p.D > (1LL << 40))
     return fail(AREA_E_UNSUPPORTED, "problem too large");
+  // the (cos, sin) tables hold max(Gh, Gw) x D/4 entries indexed in 32 bits
+  if (p.Gh > kMaxGridSide || p.Gw > kMaxGridSide)
+    return fail(AREA_E_UNSUPPORTED, pstr("grid sides must be at most 65536, max side", std::max(p.Gh, p.Gw)));
   if (p.Gh % 2 || p.Gw % 2) return fail(AREA_E_SHAPE, "both grid sides must be even");
   if (canvas_gated(p)) return AREA_OK;  // full attention only; the knobs below are unused
   int fl = p.f_min > 2 ? p.f_min : 2;

@@ -17,6 +17,7 @@ int fail(int status, const std::string& msg);
 
 // ------------------------------------------------------- fixed constants --
 constexpr int kMaxAxisWindows = 64;    // base windows per axis (kernel-argument table)
+constexpr int kMaxGridSide = 65536;    // tokens per grid side (RoPE table rows)
 constexpr int kAttnQG = 1;             // 32-query groups per attention wave
 constexpr int kAttnWaves = 8;          // waves per attention work-group
 constexpr int kAttnBM = 32 * kAttnQG * kAttnWaves;  // queries per attention work item

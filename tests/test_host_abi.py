@@ -132,6 +132,8 @@ def test_gated_canvas_keeps_full_attention():
     (dict(w_start=60, w_min=64), -2), (dict(w_min=63), -2), (dict(bridge_k=3 * 1024 * 1024), -2),
     (dict(pool_mode=7), -1), (dict(split_den=0), -1), (dict(halo=-1), -1), (dict(B=0), -1),
     (dict(f0=5), -2), (dict(rope_theta=-1.0), -1),
+    (dict(Gh=65538, Gw=2), -3),                     # a grid side above 65536 (RoPE table rows)
+    (dict(Gh=65536, Gw=16, p2_steps=0), 0),         # the largest side, Phase I only
 ])
 def test_validation_statuses(over, status):
     p = prob("flux-2048", **over)
