@@ -28,7 +28,8 @@
  *    (2k, 2k+1) of an axis half turns by pos * theta^(-4k/D)).
  *  * The attention MFMAs take IEEE fp16 operands (rotated Q and K, V and
  *    the probabilities P; three mantissa bits finer than bf16, same rate)
- *    with fp32 accumulation; the library converts into workspace.  Entries
+ *    with fp32 accumulation; the library converts keys and values into
+ *    workspace and queries in registers as they are loaded.  Entries
  *    of q, k and v must therefore stay below 32768 in magnitude.
  *  * The library never allocates device memory.  Calls that need scratch
  *    take a caller-provided workspace of at least area_workspace_bytes()
@@ -36,7 +37,10 @@
  *  * Every device call validates its arguments on the host first; on any
  *    error it returns a negative status and launches nothing.  On success
  *    it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
- *    stream) and returns without synchronising.  A failed launch returns
+ *    stream) and returns without synchronising.  The computing calls
+ *    (area_pool_kv through area_attn_step) allocate, clear and copy
+ *    nothing, so a caller may capture them (a whole step included) into a
+ *    HIP graph and replay it.  A failed launch returns
  *    AREA_E_HIP.  area_last_error() gives a per-thread description of the
  *    last failure.
  *  * Calls are re-entrant: no global mutable state other than the

@@ -266,6 +266,11 @@ def _need(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _nbytes(t) -> int:
+    """Size in bytes of a device buffer tensor (0 for None)."""
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def workspace(p: Problem, op: int, device="cuda"):
     """A device workspace tensor of the size the library asks for (or None)."""
     torch = _torch()
@@ -301,7 +306,7 @@ def area_coarse_attn(p: Problem, f: int, q, kp, vp, out=None, ws=None):
     ws = workspace(p, OP_COARSE, q.device) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_coarse_attn(ref, f, _ptr(q), _ptr(kp), _ptr(vp), _ptr(out), _ptr(ws),
-                                  0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+                                  _nbytes(ws), _stream()))
     return out
 
 
@@ -342,7 +347,7 @@ def area_window_plan(p: Problem, step: int, energy_q, k, plan=None, wsum=None, b
     s, ref = _pp(p)
     _check(lib().area_window_plan(ref, step, _ptr(energy_q), _ptr(k), _ptr(plan), _ptr(wsum),
                                   _ptr(bridge_idx) if use_bridge else None, _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream()))
+                                  _nbytes(ws), _stream()))
     return plan, wsum, (bridge_idx if use_bridge else None)
 
 
@@ -361,7 +366,7 @@ def area_window_attn(p: Problem, step: int, plan, wsum, bridge_idx, q, k, v, out
     s, ref = _pp(p)
     _check(lib().area_window_attn(ref, step, _ptr(plan), _ptr(wsum), _ptr(bridge_idx), _ptr(q),
                                   _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream()))
+                                  _nbytes(ws), _stream()))
     return out
 
 
@@ -376,7 +381,7 @@ def area_text_attn(p: Problem, q, k, v, out=None, ws=None):
     ws = workspace(p, OP_FULL, q.device) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_text_attn(ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
-                                0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+                                _nbytes(ws), _stream()))
     return out
 
 
@@ -397,7 +402,7 @@ def area_attn_step(p: Problem, step: int, latent, q, k, v, out=None, ws=None):
     ws = workspace(p, OP_STEP, q.device) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_attn_step(ref, step, C, _ptr(latent), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
-                                0 if ws is None else ws.numel() * ws.element_size(), _stream()))
+                                _nbytes(ws), _stream()))
     return out
 
 
@@ -411,7 +416,7 @@ def area_full_attn(p: Problem, q, k, v, out=None, ws=None):
     ws = workspace(p, OP_FULL, q.device) if ws is None else ws
     s, ref = _pp(p)
     _check(lib().area_full_attn(ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws),
-                                0 if ws is None else ws.numel(), _stream()))
+                                _nbytes(ws), _stream()))
     return out
 
 
