@@ -30,11 +30,15 @@
 //    tile j while the VALU sums P and takes the maximum of tile j+1.
 //    sched_group_barrier interleaves the two instruction streams, so the
 //    softmax runs in the shadow of the MFMAs instead of after them.
-//  * Eight waves of 32 queries (256 queries per work-group) use ~230
+//  * Eight waves of 32 queries (256 queries per work-group) use ~240
 //    VGPRs: one work-group per CU, two waves per SIMD, and one K/V tile DMA
 //    serves 256 queries.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
-//    only moves when a score exceeds it by more than 2^8.
+//    only moves when a score exceeds it by more than 8 (P < 2^8 in fp16).
+//    The queries carry log2(e)/sqrt(D) and each score accumulator starts
+//    from -m, so the MFMA emits scores relative to the maximum and the
+//    softmax is one exp2 and half a packed conversion per score; the exp2
+//    go to the transcendental issue class, paired two per MFMA.
 //  * Work items are mapped XCD-aware: consecutive items (same head, same
 //    window) land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -80,16 +84,17 @@ __device__ inline u16 bf_to_f16(u16 b) {
 
 // Two-axis RoPE of one 16-byte chunk (8 bf16 channels, 4 rotation pairs)
 // into fp16: c01, c23 hold the chunk's four (cos, sin) pairs, interleaved.
-// Pair (a, b) becomes (a cos - b sin, a sin + b cos), rounded to nearest.
-__device__ inline u32x4 rope8_f16(const u32x4 raw, const float4 c01, const float4 c23) {
+// Pair (a, b) becomes (a cos - b sin, a sin + b cos) times `scale`, rounded
+// to nearest.
+__device__ inline u32x4 rope8_f16(const u32x4 raw, const float4 c01, const float4 c23, const float scale = 1.0f) {
   const float co[4] = {c01.x, c01.z, c23.x, c23.z};
   const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float a = __uint_as_float(raw[j] << 16), b = __uint_as_float(raw[j] & 0xFFFF0000u);
-    const _Float16 x0 = (_Float16)(a * co[j] - b * sn[j]);
-    const _Float16 x1 = (_Float16)(a * sn[j] + b * co[j]);
+    const _Float16 x0 = (_Float16)((a * co[j] - b * sn[j]) * scale);
+    const _Float16 x1 = (_Float16)((a * sn[j] + b * co[j]) * scale);
     r[j] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
   }
   return r;
@@ -492,37 +497,21 @@ __device__ __attribute__((always_inline)) inline float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Running maximum after one more tile (exp2 units, lazy: it only moves when
-// a score exceeds it by more than 2^kLazy); alpha = factor for O and l.
-template <int QG>
-__device__ __attribute__((always_inline)) inline void tile_max(const f32x16 (&s)[QG][2], float c,
-                                                               float (&m_run)[QG], float (&alpha)[QG]) {
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    float mx = fmaxf(s[g][0][0], s[g][0][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[g][kb][i]);
-    mx = pair_max(mx);
-    const float mc = mx * c;
-    const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
-    alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-    m_run[g] = m_new;
-  }
-}
-
-// Operand fragments are read from LDS kFragAhead MFMAs before their use;
-// each MFMA of phase A is paired with kValuA VALU instructions of the
-// softmax (per two scores), each MFMA of phase B with kValuB.
+// Operand fragments are read from LDS kFragAhead MFMAs before their use.
+// Each MFMA of phase A is paired with the softmax work of two scores: two
+// exp2 (transcendental unit) and one fp16 pair conversion; each MFMA of
+// phase B with kValuB VALU instructions (P sums, next tile's maximum).
 constexpr int kFragAhead = 3;
-constexpr int kValuA = 5;
+constexpr int kTransA = 2;
+constexpr int kValuA = 1;
 constexpr int kValuB = 3;
 
-// sched_group_barrier masks
+// sched_group_barrier masks (VALU excludes the transcendental instructions,
+// which have their own class)
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedTrans = 0x400;
 
 __device__ __attribute__((always_inline)) inline const u16* uniform_ptr(const u16* p) {
   const unsigned long long v = (unsigned long long)p;
@@ -537,12 +526,15 @@ __device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage
 
 // Phase A of one step: S^T of the next tile for the wave's QG query groups
 // (2 D/16 K fragments, each read once from LDS and used by every group)
-// while the VALU turns the current scores into fp16 P^T.
+// while the VALU turns the current scores into fp16 P^T = exp2(scores).
+// Scores are in log2 units relative to the running maximum m: the queries
+// carry log2(e)/sqrt(D), and the first MFMA of each accumulator starts from
+// nm = -m instead of zero, so no per-score scale or subtraction is left.
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2], const u16* ks, int n, int hi,
                                                               const f16x8 (&qf)[QG][D / 16],
-                                                              const f32x16 (&sc)[QG][2], float c,
-                                                              const float (&negm)[QG], f16x8 (&pf)[QG][4]) {
+                                                              const f32x16 (&sc)[QG][2], const f32x16 (&nm)[QG],
+                                                              f16x8 (&pf)[QG][4]) {
   constexpr int NT = 2 * (D / 16);
   constexpr int EPM = 32 * QG / NT;  // scores turned into P per fragment
   constexpr int PF = kFragAhead;
@@ -551,27 +543,26 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
     const int kd = j >> 1, kb = j & 1;
     return (32 * kb + n) * D + (((2 * kd + hi) ^ sw) * 8);
   };
-#pragma unroll
-  for (int g = 0; g < QG; ++g)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sn[g][kb][i] = 0.0f;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   f16x8 fr[PF];
 #pragma unroll
   for (int j = 0; j < PF; ++j) fr[j] = lds_frag(ks, koff(j));
-  _Float16 ph[QG][32];
+  f16x2 ph[QG][16];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const f16x8 f = fr[j % PF];
     if (j + PF < NT) fr[j % PF] = lds_frag(ks, koff(j + PF));
 #pragma unroll
     for (int g = 0; g < QG; ++g)
-      sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], sn[g][j & 1], 0, 0, 0);
+      sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
+    // P of EPM scores, converted in pairs (one packed conversion per pair)
 #pragma unroll
-    for (int e = EPM * j; e < EPM * j + EPM; ++e) {
+    for (int e = EPM * j; e < EPM * j + EPM; e += 2) {
       const int g = e >> 5, x = e & 31;
-      ph[g][x] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[g][x >> 4][x & 15], c, negm[g]));
+      const f32x2 p2 = {__builtin_amdgcn_exp2f(sc[g][x >> 4][x & 15]),
+                        __builtin_amdgcn_exp2f(sc[g][(x + 1) >> 4][(x + 1) & 15])};
+      ph[g][x >> 1] = __builtin_convertvector(p2, f16x2);
     }
   }
 #pragma unroll
@@ -579,15 +570,19 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[g][r][i] = ph[g][8 * r + i];
+      for (int i = 0; i < 4; ++i) {
+        pf[g][r][2 * i] = ph[g][4 * r + i][0];
+        pf[g][r][2 * i + 1] = ph[g][4 * r + i][1];
+      }
   // issue order: the first PF reads, then per fragment its MFMAs, the next
-  // read and the VALU work of EPM scores
+  // read, the exp2 of EPM scores and the conversion of the previous pair
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
     if (j + PF < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuA * EPM / 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedTrans, kTransA * EPM / 2, 0);
+    if (j > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuA * EPM / 2, 0);
   }
 }
 
@@ -750,11 +745,13 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   const float c = a.c;
 
   f32x16 o[QG][DB];
-  float m_run[QG], l_run[QG];
+  f32x16 nm[QG];  // -m, the running maximum (log2 units), in all 16 registers
+  float l_run[QG];
+  float dlt[QG];  // how far the maximum moves before the next tile's P
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    m_run[g] = -INFINITY;
     l_run[g] = 0.0f;
+    dlt[g] = 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -771,20 +768,26 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
       __attribute__((always_inline)) {
     bool resc = false;
 #pragma unroll
-    for (int g = 0; g < QG; ++g) resc |= alpha[g] != 1.0f;
+    for (int g = 0; g < QG; ++g) resc |= dlt[g] != 0.0f;
     if (__any(resc)) {
+      // the maximum moved up by dlt: rescale O, and move the pending scores
+      // and the accumulator start to the new maximum
 #pragma unroll
-      for (int g = 0; g < QG; ++g)
+      for (int g = 0; g < QG; ++g) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha[g];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          scur[g][0][i] -= dlt[g];
+          scur[g][1][i] -= dlt[g];
+          nm[g][i] -= dlt[g];
+        }
+      }
     }
     f16x8 pf[QG][4];
-    float negm[QG];
-#pragma unroll
-    for (int g = 0; g < QG; ++g) negm[g] = -m_run[g];
-    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, c, negm, pf);
+    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf);
     // keep P's computation in this block: its only use is after the branch
 #pragma unroll
     for (int g = 0; g < QG; ++g) asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]));
@@ -795,10 +798,11 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       l_run[g] = l_run[g] * alpha[g] + psum[g];
-      const float mc = pair_max(mx[g]) * c;
-      const float m_new = mc > m_run[g] + kLazy ? mc : m_run[g];
-      alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-      m_run[g] = m_new;
+      // the next tile's scores are relative to the current maximum; it moves
+      // only when they exceed it by more than kLazy (P stays below 2^kLazy)
+      const float mt = pair_max(mx[g]);
+      dlt[g] = mt > kLazy ? mt : 0.0f;
+      alpha[g] = __builtin_amdgcn_exp2f(-dlt[g]);
     }
   };
 
@@ -822,12 +826,28 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   for (int g = 0; g < QG; ++g)
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1]));
+      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c));
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   tile_scores<D, QG>(sa, ks0, n, hi, qf);
   if (nkv < BN) mask_tail<QG>(sa, nkv, hi);
-  tile_max<QG>(sa, c, m_run, alpha);
+  // the first tile sets the running maximum (every query has a key there)
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    float mx = fmaxf(sa[g][0][0], sa[g][0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[g][kb][i]);
+    const float m0 = pair_max(mx);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sa[g][0][i] -= m0;
+      sa[g][1][i] -= m0;
+      nm[g][i] = -m0;
+    }
+    alpha[g] = 1.0f;
+  }
   __syncthreads();
   for (int j = 0; j < nt; j += 2) {
     issue_k<D>(ks0, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
