@@ -397,6 +397,23 @@ __device__ __attribute__((always_inline)) inline int key_perm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// LDS element offset of phase A's K fragment j (block kb = j & 1 of 32
+// keys, 16-channel step j >> 1).
+template <int D>
+__device__ __attribute__((always_inline)) inline int k_frag_off(int j, int n, int hi) {
+  const int kd = j >> 1, kb = j & 1;
+  return (32 * kb + n) * D + (((2 * kd + hi) ^ swz<D * 2>(n)) * 8);
+}
+
+// LDS element offset of phase B's V^T fragment j (block db = j % (D/32) of
+// 32 d-rows, 16-key step j / (D/32)).
+template <int D>
+__device__ __attribute__((always_inline)) inline int vt_frag_off(int j, int n, int hi) {
+  constexpr int DB = D / 32;
+  const int ks = j / DB, db = j % DB;
+  return (32 * db + n) * BN + (((2 * ks + hi) ^ swz<BN * 2>(n)) * 8);
+}
+
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Work-group of the attention kernel: kAttnWaves waves of 32 kAttnQG queries.
@@ -527,6 +544,9 @@ __device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage
 // Phase A of one step: S^T of the next tile for the wave's QG query groups
 // (2 D/16 K fragments, each read once from LDS and used by every group)
 // while the VALU turns the current scores into fp16 P^T = exp2(scores).
+// The caller has read the first kFragAhead K fragments (fr); the reads that
+// would run past the last K fragment fetch phase B's first V^T fragments
+// (vfr) instead, so phase B starts without waiting for LDS.
 // Scores are in log2 units relative to the running maximum m: the queries
 // carry log2(e)/sqrt(D), and the first MFMA of each accumulator starts from
 // nm = -m instead of zero, so no per-score scale or subtraction is left.
@@ -534,25 +554,19 @@ template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2], const u16* ks, int n, int hi,
                                                               const f16x8 (&qf)[QG][D / 16],
                                                               const f32x16 (&sc)[QG][2], const f32x16 (&nm)[QG],
-                                                              f16x8 (&pf)[QG][4]) {
+                                                              f16x8 (&pf)[QG][4], f16x8 (&fr)[kFragAhead],
+                                                              const u16* vt, f16x8 (&vfr)[kFragAhead]) {
   constexpr int NT = 2 * (D / 16);
   constexpr int EPM = 32 * QG / NT;  // scores turned into P per fragment
   constexpr int PF = kFragAhead;
-  const int sw = swz<D * 2>(n);
-  auto koff = [&](int j) __attribute__((always_inline)) {
-    const int kd = j >> 1, kb = j & 1;
-    return (32 * kb + n) * D + (((2 * kd + hi) ^ sw) * 8);
-  };
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  f16x8 fr[PF];
-#pragma unroll
-  for (int j = 0; j < PF; ++j) fr[j] = lds_frag(ks, koff(j));
   f16x2 ph[QG][16];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const f16x8 f = fr[j % PF];
-    if (j + PF < NT) fr[j % PF] = lds_frag(ks, koff(j + PF));
+    if (j + PF < NT) fr[j % PF] = lds_frag(ks, k_frag_off<D>(j + PF, n, hi));
+    else vfr[j + PF - NT] = lds_frag(vt, vt_frag_off<D>(j + PF - NT, n, hi));
 #pragma unroll
     for (int g = 0; g < QG; ++g)
       sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
@@ -574,40 +588,33 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
         pf[g][r][2 * i] = ph[g][4 * r + i][0];
         pf[g][r][2 * i + 1] = ph[g][4 * r + i][1];
       }
-  // issue order: the first PF reads, then per fragment its MFMAs, the next
-  // read, the exp2 of EPM scores and the conversion of the previous pair
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+  // issue order: per fragment its MFMAs, the next read (K, then V^T for
+  // phase B), the exp2 of EPM scores and the conversion of the previous pair
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
-    if (j + PF < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedTrans, kTransA * EPM / 2, 0);
     if (j > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuA * EPM / 2, 0);
   }
 }
 
 // Phase B of one step: O^T += V^T P^T for every group (4 D/32 V^T
-// fragments, each read once) while the VALU sums P and takes the next
-// tile's per-lane maxima.
+// fragments, each read once; the first kFragAhead already in fr) while the
+// VALU sums P and takes the next tile's per-lane maxima.
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
                                                               const f16x8 (&pf)[QG][4], const f32x16 (&sn)[QG][2],
-                                                              float (&psum)[QG], float (&mx)[QG]) {
+                                                              float (&psum)[QG], float (&mx)[QG],
+                                                              f16x8 (&fr)[kFragAhead]) {
   constexpr int DB = D / 32;
   constexpr int NT = 4 * DB;
   constexpr int PF = kFragAhead;
-  const int sw = swz<BN * 2>(n);
-  auto voff = [&](int j) __attribute__((always_inline)) {
-    const int ks = j / DB, db = j % DB;
-    return (32 * db + n) * BN + (((2 * ks + hi) ^ sw) * 8);
-  };
-  f16x8 fr[PF];
-#pragma unroll
-  for (int j = 0; j < PF; ++j) fr[j] = lds_frag(vt, voff(j));
+
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const f16x8 f = fr[j % PF];
-    if (j + PF < NT) fr[j % PF] = lds_frag(vt, voff(j + PF));
+    if (j + PF < NT) fr[j % PF] = lds_frag(vt, vt_frag_off<D>(j + PF, n, hi));
 #pragma unroll
     for (int g = 0; g < QG; ++g)
       o[g][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, pf[g][j / DB], o[g][j % DB], 0, 0, 0);
@@ -632,7 +639,6 @@ __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D 
       for (int i = 0; i < 16; ++i) m = fmaxf(m, sn[g][kb][i]);
     mx[g] = m;
   }
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
@@ -766,6 +772,12 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   // j+2 and V tile j+1 stream into the other stages meanwhile.
   auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j)
       __attribute__((always_inline)) {
+    // phase A's first K fragments, read ahead of the rescale test so their
+    // LDS latency overlaps it
+    f16x8 kfr[kFragAhead];
+#pragma unroll
+    for (int jj = 0; jj < kFragAhead; ++jj)
+      kfr[jj] = lds_frag(ksn, k_frag_off<D>(jj, n, hi));
     bool resc = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) resc |= dlt[g] != 0.0f;
@@ -787,14 +799,15 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
       }
     }
     f16x8 pf[QG][4];
-    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf);
+    f16x8 vfr[kFragAhead];
+    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr);
     // keep P's computation in this block: its only use is after the branch
 #pragma unroll
     for (int g = 0; g < QG; ++g) asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]));
     const int valid = nkv - (j + 1) * BN;
     if (valid < BN) mask_tail<QG>(snext, valid, hi);
     float psum[QG], mx[QG];
-    phase_b<D, QG>(o, vtc, n, hi, pf, snext, psum, mx);
+    phase_b<D, QG>(o, vtc, n, hi, pf, snext, psum, mx, vfr);
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       l_run[g] = l_run[g] * alpha[g] + psum[g];
