@@ -277,3 +277,54 @@ def test_single_token_pooling_2048(flux2048, mode):
         for h in (0, 13):
             _, vp_ref = O.pool_kv(kh[:, h:h + 1], vh[:, h:h + 1], wl.Gh, wl.Gw, f, mode, wl.rope_theta, seed=5)
             np.testing.assert_array_equal(got[:, h:h + 1], vp_ref.astype(np.float16), f"f={f} head {h}")
+
+
+# ------------------------------------------------ running-maximum moves --
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_running_maximum_moves(direction):
+    """Scores that climb along the key sequence make every later tile exceed
+    the running maximum by far more than the lazy headroom of 8 (log2 units),
+    so the rescale path (O and l rescaled, pending scores and accumulator start
+    moved) runs on almost every tile; falling scores keep the first tile's
+    maximum.  The ramp sits on the lowest-frequency rotation pair of the row
+    half, which RoPE barely turns on a 32 x 32 grid: q carries 8 there, k the
+    ramp 0 .. 256 (about 23 log2 units per 64-key tile)."""
+    wl = W.get("tiny-32")
+    p = A.problem_for(wl)
+    q, k, v = W.make_qkv(wl, device="cpu", dtype="bf16")
+    N, D = wl.N, wl.D
+    ch = D // 2 - 2
+    j = torch.arange(N, dtype=torch.float32)
+    ramp = 256.0 * (j if direction == "rising" else (N - 1 - j)) / N
+    q[..., ch] = 8.0
+    q[..., ch + 1] = 0.0
+    k[..., ch] = ramp.to(torch.bfloat16)
+    k[..., ch + 1] = 0.0
+    # the outputs nearly copy single value rows here, so their bf16 rounding
+    # sets the error floor: halve V (exact in bf16) to keep clear of the bound
+    v = v * 0.5
+    qh, kh, vh = to_host(q), to_host(k), to_host(v)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    full = A.area_full_attn(p, q, k, v)
+    f = A.area_step_info(p, 0)["f"]
+    kp, vp = A.area_pool_kv(p, f, k, v)
+    co = A.area_coarse_attn(p, f, q, kp, vp)
+    lat = W.make_latent(wl)
+    _, Eq = A.area_dwt_detail(p, torch.from_numpy(lat).cuda())
+    s = wl.p1_steps
+    plan, wsum, br = A.area_window_plan(p, s, Eq, k)
+    win = A.area_window_attn(p, s, plan, wsum, br, q, k, v)
+    torch.cuda.synchronize()
+    assert_close(to_host(full), O.full_attention(qh, kh, vh, wl.Gh, wl.Gw, wl.rope_theta),
+                 f"full attention, {direction} scores")
+    kpr, vpr = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, O.POOL_MEAN, wl.rope_theta)
+    assert_close(to_host(co), O.coarse_attention(qh, kpr, vpr, wl.Gh, wl.Gw, f, wl.rope_theta),
+                 f"coarse attention f={f}, {direction} scores")
+    Eq_ref = O.energy_fixed(O.detail_energy(lat))
+    w0 = O.window_sizes(wl.w_start, wl.w_min, wl.p2_steps)[0]
+    ref = O.window_plan(wl.Gh, wl.Gw, w0, wl.halo, wl.seed, 0, Eq_ref)
+    br_ref = O.bridge_all(kh, wl.bridge_k, wl.Gh, wl.Gw)
+    np.testing.assert_array_equal(br.cpu().numpy(), br_ref)
+    assert_close(to_host(win), O.window_attention(qh, kh, vh, ref, br_ref, wl.Gh, wl.Gw, wl.rope_theta),
+                 f"window attention w={w0}, {direction} scores")
