@@ -770,14 +770,24 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   // they compute O += P V for tile j, the VALU sums P and takes the maximum
   // of tile j+1.  K tile j+1 and V tile j are resident during step j; K tile
   // j+2 and V tile j+1 stream into the other stages meanwhile.
-  auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // the buffer resources below need wave-uniform bases and sizes
+  kbase = uniform_ptr(kbase);
+  vtbase = uniform_ptr(vtbase);
+  nkv = __builtin_amdgcn_readfirstlane(nkv);
+  auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j,
+                  u16* kdma, int ktile, u16* vdma, int vtile)
       __attribute__((always_inline)) {
-    // phase A's first K fragments, read ahead of the rescale test so their
-    // LDS latency overlaps it
+    // phase A's first K fragments, read ahead of the tile DMAs and the
+    // rescale test so their LDS latency overlaps both
     f16x8 kfr[kFragAhead];
 #pragma unroll
     for (int jj = 0; jj < kFragAhead; ++jj)
       kfr[jj] = lds_frag(ksn, k_frag_off<D>(jj, n, hi));
+    __builtin_amdgcn_sched_barrier(0);
+    // DMAs of the next tiles into the two free stages
+    issue_k<D>(kdma, ktile, tid, wave_u, nkv, kbase);
+    issue_v<D>(vdma, vtile, tid, wave_u, vtbase);
     bool resc = false;
 #pragma unroll
     for (int g = 0; g < QG; ++g) resc |= dlt[g] != 0.0f;
@@ -819,17 +829,12 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     }
   };
 
-  // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each
-  // half-iteration first starts the DMAs into the two free stages, then
+  // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each step
+  // reads its first K fragments, starts the DMAs into the two free stages,
   // computes, then waits for its own DMAs and syncs.  No DMA is outstanding
   // at a branch merge; the last half-iteration re-loads clamped tiles instead
   // of branching around the DMA, and its scores of the tile past the end are
   // never used.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // the buffer resources below need wave-uniform bases and sizes
-  kbase = uniform_ptr(kbase);
-  vtbase = uniform_ptr(vtbase);
-  nkv = __builtin_amdgcn_readfirstlane(nkv);
   f32x16 sa[QG][2], sb[QG][2];
   issue_k<D>(ks0, 0, tid, wave_u, nkv, kbase);
   issue_v<D>(vt0, 0, tid, wave_u, vtbase);
@@ -863,15 +868,11 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   }
   __syncthreads();
   for (int j = 0; j < nt; j += 2) {
-    issue_k<D>(ks0, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
-    issue_v<D>(vt1, min(j + 1, nt - 1), tid, wave_u, vtbase);
-    step(sa, sb, ks1, vt0, j);
+    step(sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     if (j + 1 >= nt) break;
-    issue_k<D>(ks1, min(j + 3, nt - 1), tid, wave_u, nkv, kbase);
-    issue_v<D>(vt0, min(j + 2, nt - 1), tid, wave_u, vtbase);
-    step(sb, sa, ks0, vt1, j + 1);
+    step(sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
   }
