@@ -257,7 +257,7 @@ def main():
                          "as configured and with splits, halo or bridge turned off, and at fixed w=64")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the AReA path runs on one GPU (no sharding across GPUs is implemented); --gpus must be 1"}))
         sys.exit(2)
 
     import torch
