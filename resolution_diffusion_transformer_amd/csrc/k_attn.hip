@@ -32,7 +32,9 @@
 //    softmax runs in the shadow of the MFMAs instead of after them.
 //  * Eight waves of 32 queries (256 queries per work-group) use ~240
 //    VGPRs: one work-group per CU, two waves per SIMD, and one K/V tile DMA
-//    serves 256 queries.
+//    serves 256 queries.  In the last, partial query tile of a window, waves
+//    with no query left only take their share of the DMAs and barriers, so
+//    the working waves have their SIMDs to themselves.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
 //    only moves when a score exceeds it by more than 8 (P < 2^8 in fp16).
 //    The queries carry log2(e)/sqrt(D) and each score accumulator starts
@@ -867,14 +869,30 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     alpha[g] = 1.0f;
   }
   __syncthreads();
-  for (int j = 0; j < nt; j += 2) {
-    step(sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
-    if (j + 1 >= nt) break;
-    step(sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    __syncthreads();
+  bool any_q = false;
+#pragma unroll
+  for (int g = 0; g < QG; ++g) any_q |= qvalid[g];
+  if (__any(any_q)) {
+    for (int j = 0; j < nt; j += 2) {
+      step(sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+      if (j + 1 >= nt) break;
+      step(sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+    }
+  } else {
+    // none of this wave's queries is in the item (the last, partial query
+    // tile of a window): it only takes its share of the same tile DMAs and
+    // the same nt barriers as the computing waves
+    for (int j = 0; j < nt; ++j) {
+      const bool even = (j & 1) == 0;
+      issue_k<D>(even ? ks0 : ks1, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
+      issue_v<D>(even ? vt1 : vt0, min(j + 1, nt - 1), tid, wave_u, vtbase);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: normalise and write
