@@ -26,8 +26,8 @@
 //    MFMA operand reads are bank-conflict free.
 //  * Each wave runs a two-phase software pipeline over key tiles: the
 //    matrix cores compute the scores of tile j+1 while the VALU turns the
-//    scores of tile j into P (exp2, fp16), then they compute O += P V for
-//    tile j while the VALU sums P and takes the maximum of tile j+1.
+//    scores of tile j into P (exp2, fp16) and sums it, then they compute
+//    O += P V for tile j.
 //    sched_group_barrier interleaves the two instruction streams, so the
 //    softmax runs in the shadow of the MFMAs instead of after them.
 //  * Eight waves of 32 queries (256 queries per work-group) use ~240
@@ -36,7 +36,9 @@
 //    with no query left only take their share of the DMAs and barriers, so
 //    the working waves have their SIMDs to themselves.
 //  * Online softmax in exp2 units with lazy rescaling: the running maximum
-//    only moves when a score exceeds it by more than 8 (P < 2^8 in fp16).
+//    only moves when a lane's P sum over a tile exceeds 2^8, which bounds
+//    every P it holds; it then moves to the tile's maximum and P is
+//    recomputed.  No per-tile maximum is taken otherwise.
 //    The queries carry log2(e)/sqrt(D) and each score accumulator starts
 //    from -m, so the MFMA emits scores relative to the maximum and the
 //    softmax is one exp2 and half a packed conversion per score; the exp2
@@ -62,7 +64,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BN = kAttnBN;
-constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
+// A lane's P sum over a tile above this (2^8) moves the running maximum.
+constexpr float kPsumMax = 256.0f;
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14,
 // expcnt[6:4], lgkmcnt[11:8]): wait for every vector memory operation.
 constexpr int kVmcnt0 = 0x0F70;
@@ -518,12 +521,12 @@ __device__ __attribute__((always_inline)) inline float pair_sum(float v) {
 
 // Operand fragments are read from LDS kFragAhead MFMAs before their use.
 // Each MFMA of phase A is paired with the softmax work of two scores: two
-// exp2 (transcendental unit) and one fp16 pair conversion; each MFMA of
-// phase B with kValuB VALU instructions (P sums, next tile's maximum).
+// exp2 (transcendental unit), then the pair's fp16 conversion and its dot2
+// into the P sum, in groups of up to kValuA VALU instructions.  Phase B's
+// MFMAs carry no softmax work.
 constexpr int kFragAhead = 3;
 constexpr int kTransA = 2;
-constexpr int kValuA = 1;
-constexpr int kValuB = 3;
+constexpr int kValuA = 3;
 
 // sched_group_barrier masks (VALU excludes the transcendental instructions,
 // which have their own class)
@@ -545,7 +548,8 @@ __device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage
 
 // Phase A of one step: S^T of the next tile for the wave's QG query groups
 // (2 D/16 K fragments, each read once from LDS and used by every group)
-// while the VALU turns the current scores into fp16 P^T = exp2(scores).
+// while the VALU turns the current scores into fp16 P^T = exp2(scores) and
+// sums each lane's P (psum).
 // The caller has read the first kFragAhead K fragments (fr); the reads that
 // would run past the last K fragment fetch phase B's first V^T fragments
 // (vfr) instead, so phase B starts without waiting for LDS.
@@ -557,13 +561,18 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
                                                               const f16x8 (&qf)[QG][D / 16],
                                                               const f32x16 (&sc)[QG][2], const f32x16 (&nm)[QG],
                                                               f16x8 (&pf)[QG][4], f16x8 (&fr)[kFragAhead],
-                                                              const u16* vt, f16x8 (&vfr)[kFragAhead]) {
+                                                              const u16* vt, f16x8 (&vfr)[kFragAhead],
+                                                              float (&psum)[QG]) {
   constexpr int NT = 2 * (D / 16);
   constexpr int EPM = 32 * QG / NT;  // scores turned into P per fragment
   constexpr int PF = kFragAhead;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   f16x2 ph[QG][16];
+  const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float ps[QG][2];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) ps[g][0] = ps[g][1] = 0.0f;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const f16x8 f = fr[j % PF];
@@ -579,8 +588,11 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
       const f32x2 p2 = {__builtin_amdgcn_exp2f(sc[g][x >> 4][x & 15]),
                         __builtin_amdgcn_exp2f(sc[g][(x + 1) >> 4][(x + 1) & 15])};
       ph[g][x >> 1] = __builtin_convertvector(p2, f16x2);
+      ps[g][(x >> 1) & 1] = __builtin_amdgcn_fdot2(ph[g][x >> 1], one2, ps[g][(x >> 1) & 1], false);
     }
   }
+#pragma unroll
+  for (int g = 0; g < QG; ++g) psum[g] = ps[g][0] + ps[g][1];
 #pragma unroll
   for (int g = 0; g < QG; ++g)
 #pragma unroll
@@ -602,13 +614,10 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
 }
 
 // Phase B of one step: O^T += V^T P^T for every group (4 D/32 V^T
-// fragments, each read once; the first kFragAhead already in fr) while the
-// VALU sums P and takes the next tile's per-lane maxima.
+// fragments, each read once; the first kFragAhead already in fr).
 template <int D, int QG>
 __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D / 32], const u16* vt, int n, int hi,
-                                                              const f16x8 (&pf)[QG][4], const f32x16 (&sn)[QG][2],
-                                                              float (&psum)[QG], float (&mx)[QG],
-                                                              f16x8 (&fr)[kFragAhead]) {
+                                                              const f16x8 (&pf)[QG][4], f16x8 (&fr)[kFragAhead]) {
   constexpr int DB = D / 32;
   constexpr int NT = 4 * DB;
   constexpr int PF = kFragAhead;
@@ -621,31 +630,10 @@ __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D 
     for (int g = 0; g < QG; ++g)
       o[g][j % DB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, pf[g][j / DB], o[g][j % DB], 0, 0, 0);
   }
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        s0 = __builtin_amdgcn_fdot2(h2{pf[g][r][i], pf[g][r][i + 1]}, one2, s0, false);
-        s1 = __builtin_amdgcn_fdot2(h2{pf[g][r][i + 2], pf[g][r][i + 3]}, one2, s1, false);
-      }
-    psum[g] = s0 + s1;
-    float m = fmaxf(sn[g][0][0], sn[g][0][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, sn[g][kb][i]);
-    mx[g] = m;
-  }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
     if (j + PF < NT) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuB * QG, 0);
   }
 }
 
@@ -755,22 +743,20 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   f32x16 o[QG][DB];
   f32x16 nm[QG];  // -m, the running maximum (log2 units), in all 16 registers
   float l_run[QG];
-  float dlt[QG];  // how far the maximum moves before the next tile's P
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     l_run[g] = 0.0f;
-    dlt[g] = 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[g][db][i] = 0.0f;
   }
 
-  float alpha[QG];
   // Software pipeline over key tiles: while the matrix cores compute the
-  // scores of tile j+1, the VALU turns the scores of tile j into P; while
-  // they compute O += P V for tile j, the VALU sums P and takes the maximum
-  // of tile j+1.  K tile j+1 and V tile j are resident during step j; K tile
+  // scores of tile j+1, the VALU turns the scores of tile j into P and sums
+  // it; then they compute O += P V for tile j.  A P sum that flags a larger
+  // score moves the maximum between the two phases (rare).  K tile j+1 and
+  // V tile j are resident during step j; K tile
   // j+2 and V tile j+1 stream into the other stages meanwhile.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // the buffer resources below need wave-uniform bases and sizes
@@ -780,8 +766,8 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j,
                   u16* kdma, int ktile, u16* vdma, int vtile)
       __attribute__((always_inline)) {
-    // phase A's first K fragments, read ahead of the tile DMAs and the
-    // rescale test so their LDS latency overlaps both
+    // phase A's first K fragments, read ahead of the tile DMAs so their LDS
+    // latency overlaps them
     f16x8 kfr[kFragAhead];
 #pragma unroll
     for (int jj = 0; jj < kFragAhead; ++jj)
@@ -790,45 +776,64 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     // DMAs of the next tiles into the two free stages
     issue_k<D>(kdma, ktile, tid, wave_u, nkv, kbase);
     issue_v<D>(vdma, vtile, tid, wave_u, vtbase);
-    bool resc = false;
+    f16x8 pf[QG][4];
+    f16x8 vfr[kFragAhead];
+    float psum[QG];
+    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr, psum);
+    // keep P's computation in this block: its only use is after the branch
 #pragma unroll
-    for (int g = 0; g < QG; ++g) resc |= dlt[g] != 0.0f;
-    if (__any(resc)) {
-      // the maximum moved up by dlt: rescale O, and move the pending scores
-      // and the accumulator start to the new maximum
+    for (int g = 0; g < QG; ++g)
+      asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]), "+v"(psum[g]));
+    // Lazy maximum: the scores were taken relative to the running maximum m,
+    // so P <= 1 unless the tile holds a larger score.  Each lane's P sum
+    // bounds every P it holds; while it stays below 2^8, P fits fp16 with
+    // room to spare and m stays.  Otherwise (rare) m moves to the tile's
+    // maximum: O and l are rescaled, P is recomputed, and the next tile's
+    // scores and the accumulator start are shifted to the new m.
+    bool big = false;
+#pragma unroll
+    for (int g = 0; g < QG; ++g) big |= !(psum[g] <= kPsumMax);
+    if (__any(big)) {
 #pragma unroll
       for (int g = 0; g < QG; ++g) {
+        float m = fmaxf(scur[g][0][0], scur[g][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, scur[g][kb][i]);
+        const float mt = pair_max(m);
+        const float dlt = mt > 0.0f ? mt : 0.0f;
+        const float alpha = __builtin_amdgcn_exp2f(-dlt);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha[g];
+          for (int i = 0; i < 16; ++i) o[g][db][i] *= alpha;
+        l_run[g] *= alpha;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          scur[g][0][i] -= dlt[g];
-          scur[g][1][i] -= dlt[g];
-          nm[g][i] -= dlt[g];
+          nm[g][i] -= dlt;
+          snext[g][0][i] -= dlt;
+          snext[g][1][i] -= dlt;
         }
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        float s0 = 0.0f;
+#pragma unroll
+        for (int x = 0; x < 32; x += 2) {
+          const f16x2 p2 = {(_Float16)__builtin_amdgcn_exp2f(scur[g][x >> 4][x & 15] - dlt),
+                            (_Float16)__builtin_amdgcn_exp2f(scur[g][(x + 1) >> 4][(x + 1) & 15] - dlt)};
+          pf[g][x >> 3][x & 7] = p2[0];
+          pf[g][x >> 3][(x & 7) + 1] = p2[1];
+          s0 = __builtin_amdgcn_fdot2(p2, one2, s0, false);
+        }
+        psum[g] = s0;
       }
     }
-    f16x8 pf[QG][4];
-    f16x8 vfr[kFragAhead];
-    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr);
-    // keep P's computation in this block: its only use is after the branch
-#pragma unroll
-    for (int g = 0; g < QG; ++g) asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]));
     const int valid = nkv - (j + 1) * BN;
     if (valid < BN) mask_tail<QG>(snext, valid, hi);
-    float psum[QG], mx[QG];
-    phase_b<D, QG>(o, vtc, n, hi, pf, snext, psum, mx, vfr);
+    phase_b<D, QG>(o, vtc, n, hi, pf, vfr);
 #pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      l_run[g] = l_run[g] * alpha[g] + psum[g];
-      // the next tile's scores are relative to the current maximum; it moves
-      // only when they exceed it by more than kLazy (P stays below 2^kLazy)
-      const float mt = pair_max(mx[g]);
-      dlt[g] = mt > kLazy ? mt : 0.0f;
-      alpha[g] = __builtin_amdgcn_exp2f(-dlt[g]);
-    }
+    for (int g = 0; g < QG; ++g) l_run[g] += psum[g];
   };
 
   // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each step
@@ -866,7 +871,6 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
       sa[g][1][i] -= m0;
       nm[g][i] = -m0;
     }
-    alpha[g] = 1.0f;
   }
   __syncthreads();
   bool any_q = false;
@@ -901,16 +905,20 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     float lt = pair_sum(l_run[g]);
     float inv = 1.0f / lt;
     if (!qvalid[g]) continue;
+    // an opaque copy of the query's row: its addresses are recomputed here
+    // rather than kept live in registers across the key loop
+    int qt = qtok[g];
+    asm volatile("" : "+v"(qt));
     bool direct = true;
     int t = 0;
     if constexpr (WIN) {
       t = qtile * BM + wave * 32 * QG + 32 * g + n;
       int uy = t / qw, ux = t - (t / qw) * qw;
       int wt = min(uy + 1, qh - uy) * min(ux + 1, qw - ux);
-      direct = a.wsum[qtok[g]] == wt;
+      direct = a.wsum[qt] == wt;
     }
     if (direct) {
-      u16* orow = a.out + (bh * (int64_t)a.q_rows + a.q0 + qtok[g]) * D;
+      u16* orow = a.out + (bh * (int64_t)a.q_rows + a.q0 + qt) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
