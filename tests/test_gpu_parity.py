@@ -284,10 +284,10 @@ def test_single_token_pooling_2048(flux2048, mode):
 @pytest.mark.parametrize("direction", ["rising", "falling"])
 def test_running_maximum_moves(direction):
     """Scores that climb along the key sequence make every later tile exceed
-    the running maximum by far more than the lazy headroom of 8 (log2 units),
-    so the rescale path (O and l rescaled, pending scores and accumulator start
-    moved) runs on almost every tile; falling scores keep the first tile's
-    maximum.  The ramp sits on the lowest-frequency rotation pair of the row
+    the running maximum by far more than 8 log2 units (a lane's P sum above
+    2^8), so the rescale path (O and l rescaled, P recomputed, pending scores
+    and accumulator start moved) runs on almost every tile; falling scores
+    keep the first tile's maximum.  The ramp sits on the lowest-frequency rotation pair of the row
     half, which RoPE barely turns on a 32 x 32 grid: q carries 8 there, k the
     ramp 0 .. 256 (about 23 log2 units per 64-key tile)."""
     wl = W.get("tiny-32")
