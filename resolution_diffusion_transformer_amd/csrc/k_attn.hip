@@ -786,7 +786,7 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
       asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]), "+v"(psum[g]));
     // Lazy maximum: the scores were taken relative to the running maximum m,
     // so P <= 1 unless the tile holds a larger score.  Each lane's P sum
-    // bounds every P it holds; while it stays below 2^8, P fits fp16 with
+    // bounds every P it holds; while it stays at most 2^8, P fits fp16 with
     // room to spare and m stays.  Otherwise (rare) m moves to the tile's
     // maximum: O and l are rescaled, P is recomputed, and the next tile's
     // scores and the accumulator start are shifted to the new m.
