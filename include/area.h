@@ -103,8 +103,8 @@ extern "C" {
  * Every q, k, v and out tensor is [B][H][T + Gh*Gw][D]: T text tokens first,
  * then the image tokens in row-major order (image token (y, x) is row
  * T + y*Gw + x).  Text tokens sit at RoPE position (0, 0), i.e. are not
- * rotated; they are never pooled (ai.info summary, Methodology, Phase I:
- * each of the N image queries attends to T + N/f^2 keys) and join every
+ * rotated; pooling leaves them out (ai.info summary, Methodology, Phase I:
+ * an image query's key set is the T text keys plus N/f^2 pooled keys) and join every
  * Phase II key set whole.  The image-query calls (area_coarse_attn,
  * area_window_attn) write the image rows of out; text queries take the dense
  * path over all T + N keys (area_text_attn).  area_full_attn writes every
@@ -148,6 +148,9 @@ typedef struct area_step {
   int64_t q_total;            /* sum of base-window query areas                  */
   int32_t R;                  /* bridge tokens per (batch, head) of a window     */
                               /* step (0: none), else 0                          */
+  int32_t bridge_rh, bridge_rw; /* the bridge's cell grid (R = rh * rw cells,    */
+                              /* the most nearly square cells in tokens); 0, 0   */
+                              /* without a bridge                                */
 } area_step;
 
 /* ---- host-only calls (no GPU needed) ------------------------------------ */
@@ -288,8 +291,12 @@ int area_dwt_detail(const area_problem* p, int C, const float* latent, float* en
  *  bridge_idx: [B][H][R] int32 sorted ascending, R = area_step_info().R of
  *          the step (p->bridge_k, or round(rho w_t)^2): per (b, h), the key
  *          farthest (sum of squared channel deviations, float64, channels in
- *          order) from the exact mean key in each of R cells of a r_h x r_w
- *          grid of the image; ties to the smaller index.
+ *          order) from the exact mean key in each of R cells of the
+ *          r_h x r_w grid of area_step_info() (bridge_rh, bridge_rw: the
+ *          factor pair of R with the most nearly square cells in tokens,
+ *          ties to fewer cell rows; cell (a, c) covers rows
+ *          [a Gh / r_h, (a+1) Gh / r_h) and columns [c Gw / r_w,
+ *          (c+1) Gw / r_w)); ties to the smaller index.
  * Workspace: area_workspace_bytes(p, AREA_OP_PLAN). */
 int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, const void* k,
                      int32_t* plan, int32_t* wsum, int32_t* bridge_idx,

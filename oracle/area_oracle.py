@@ -26,8 +26,9 @@ Sources (page titles, sections):
 Where the pages leave a step open, the reading taken is marked READING and
 named (R1...R23); each is one small function here.
 
-Text tokens (READING R20, [summary] Phase I: text tokens are never pooled,
-so each of the N image queries attends to T + N/f^2 keys): with T > 0 the
+Text tokens (READING R20, [summary] Phase I: pooling leaves the text
+tokens alone, so a query's key set is the T text keys plus the N/f^2
+pooled image keys): with T > 0 the
 token sequence is T text tokens first, then the Gh*Gw image tokens in
 row-major order.  Text tokens sit at RoPE position (0, 0) (no rotation),
 join every key set of both phases whole, and text queries attend densely to
@@ -236,7 +237,8 @@ def pool_kv(k, v, Gh: int, Gw: int, f: int, mode: int, theta: float, T: int = 0,
     modes take one token of the block, the same token for K and V (its
     offset from pool_offsets; medoid chooses it on the keys).  With T text
     tokens, the T text keys (position (0, 0): unrotated) and values come
-    first, unpooled ([summary] Phase I: text tokens are never pooled)."""
+    first, unpooled ([summary] Phase I: pooling applies to image tokens
+    only)."""
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     ki, vi = k[..., T:, :], v[..., T:, :]
@@ -338,9 +340,9 @@ def window_sizes(w_start: int, w_min: int, steps: int) -> List[int]:
 
 def w_start_auto(Gh: int, Gw: int, w_min: int) -> int:
     """READING R7 of the first Phase II window ([summary] Phase II: the
-    largest window for which windowed attention is still cheaper than a
-    full-attention pass, about 70% of the longer side; [blog] Fase II, same
-    rule): the largest even w in [w_min, max(Gh, Gw)] whose base tiling
+    first window is the biggest one whose windowed attention costs less than
+    one pass of full attention, near 70% of the grid's longer side; [blog]
+    Fase II gives the same rule): the largest even w in [w_min, max(Gh, Gw)] whose base tiling
     costs fewer (query, key) pairs than full attention, each window attending
     to itself: sum over the R8 windows of (min(w, Gh) * min(w, Gw))^2 <
     (Gh * Gw)^2.  w_min when no larger size qualifies."""
@@ -603,19 +605,27 @@ def window_plan(Gh: int, Gw: int, w: int, halo: int, seed: int, step: int,
 
 
 def bridge_cells(R: int, Gh: int, Gw: int) -> Tuple[int, int]:
-    """READING R13 (spatial spread): R cells on an r_h x r_w grid, r_h the
-    largest divisor of R with r_h^2 * Gw <= R * Gh (closest to the grid's
-    aspect ratio from below)."""
+    """READING R13 (spatial spread, [summary] Phase II): the bridge takes one
+    token from each cell of an r_h x r_w grid of R = r_h * r_w cells.  Among
+    the factor pairs of R with r_h <= Gh and r_w <= Gw, the cells are the
+    most nearly square in tokens: a cell is (Gh / r_h) x (Gw / r_w) tokens, so
+    its elongation is max(Gh r_w, Gw r_h) / min(Gh r_w, Gw r_h), compared
+    exactly as integer cross products; equal elongations go to the smaller
+    r_h (fewer, taller cell rows).  No pair fits: ValueError."""
     best = None
-    for d in range(1, R + 1):
-        if R % d == 0 and d * d * Gw <= R * Gh:
-            best = d
+    for rh in range(1, R + 1):
+        if R % rh:
+            continue
+        rw = R // rh
+        if rh > Gh or rw > Gw:
+            continue
+        a, b = Gh * rw, Gw * rh           # cell height : cell width = a : b
+        hi, lo = max(a, b), min(a, b)
+        if best is None or hi * best[1] < best[0] * lo:
+            best = (hi, lo, rh, rw)
     if best is None:
-        raise ValueError("bridge size")
-    rh, rw = best, R // best
-    if rh > Gh or rw > Gw:
-        raise ValueError("more bridge cells than grid rows or columns")
-    return rh, rw
+        raise ValueError("no r_h x r_w = R cell grid fits the token grid")
+    return best[2], best[3]
 
 
 def bridge_scores(kbh: np.ndarray) -> np.ndarray:
@@ -746,9 +756,9 @@ PHASE_FULL, PHASE_COARSE, PHASE_WINDOW = 0, 1, 2
 
 def canvas_check(Gh: int, Gw: int, native_h: int, native_w: int, f_min: int = 2) -> int:
     """[readme] canvas-rules paragraph and [blog] "Cómo entra en tu
-    pipeline": a canvas at or below the native size keeps the original
-    (full) attention; otherwise both patch counts must share a factor of at
-    least 2 for the f x f pooling.  Returns PHASE_FULL for the gated case and
+    pipeline": a canvas no larger than the native one runs the model's own
+    (full) attention; a larger one needs patch counts along the two sides
+    with a common factor >= 2, because Phase I pools square f x f blocks.  Returns PHASE_FULL for the gated case and
     -1 when the grid cannot be pooled, else PHASE_COARSE."""
     if Gh <= native_h and Gw <= native_w:
         return PHASE_FULL
@@ -777,16 +787,3 @@ def phase1_steps_for_sigma(sigmas: Sequence[float], sigma_star: float) -> int:
             break
         n += 1
     return n
-
-
-# ----------------------------------------------------------------------------
-# Work counts (for measurement)
-# ----------------------------------------------------------------------------
-
-
-def window_pairs(plan: Plan, bridge_bh: Optional[np.ndarray], Gw: int) -> int:
-    """Sum over windows of |queries| * |keys| for one (batch, head)."""
-    tot = 0
-    for win in plan.windows:
-        tot += win.qh * win.qw * len(window_key_indices(win, Gw, bridge_bh))
-    return tot

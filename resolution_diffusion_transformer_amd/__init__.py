@@ -60,7 +60,8 @@ class _Step(ctypes.Structure):
     _fields_ = [("phase", ctypes.c_int32), ("f", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("ny", ctypes.c_int32), ("nx", ctypes.c_int32), ("jit_y", ctypes.c_int32),
                 ("jit_x", ctypes.c_int32), ("max_windows", ctypes.c_int32),
-                ("q_total", ctypes.c_int64), ("R", ctypes.c_int32)]
+                ("q_total", ctypes.c_int64), ("R", ctypes.c_int32),
+                ("bridge_rh", ctypes.c_int32), ("bridge_rw", ctypes.c_int32)]
 
 
 @dataclass

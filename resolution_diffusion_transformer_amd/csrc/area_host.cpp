@@ -91,8 +91,8 @@ void base_starts(int G, int w, std::vector<int>& out) {
 static int64_t axis_count(int G, int w) { return w >= G ? 1 : (G + w - 1) / w; }
 
 // READING R7 (ai.info summary, Methodology, Phase II; blog, Fase II: the
-// first window is the largest for which windowed attention is still cheaper
-// than one full-attention pass, about 70% of the longer side): with
+// first window is the biggest whose windowed attention costs less than one
+// pass of full attention, near 70% of the longer side): with
 // p.w_start == 0, the largest even w in [w_min, max(Gh, Gw)] whose base
 // tiling, each window attending to itself, has fewer (query, key) pairs than
 // full attention: n_y n_x (min(w,Gh) min(w,Gw))^2 < (Gh Gw)^2, compared in
@@ -173,17 +173,35 @@ bool axis_tiling(int G, int w, uint64_t seed, int t, int axis, AxisTiling& out) 
   return true;
 }
 
-// READING R13 (ai.info summary, Phase II: bridge tokens are spread
-// spatially): R cells on r_h x r_w, r_h the largest divisor of R with
-// r_h^2 Gw <= R Gh.
+// READING R13 (ai.info summary, Phase II: bridge tokens are spread over the
+// image): one token per cell of an r_h x r_w = R grid.  Among the factor
+// pairs with r_h <= Gh and r_w <= Gw the cells, (Gh / r_h) x (Gw / r_w)
+// tokens, are the most nearly square: elongation max(Gh r_w, Gw r_h) /
+// min(Gh r_w, Gw r_h), compared as exact 128-bit cross products; equal
+// elongations go to the smaller r_h.  false when no pair fits.
 bool bridge_cells(int R, int Gh, int Gw, int& rh, int& rw) {
-  int best = -1;
-  for (int d = 1; d <= R; ++d)
-    if (R % d == 0 && (long long)d * d * Gw <= (long long)R * Gh) best = d;
-  if (best < 0) return false;
-  rh = best;
-  rw = R / best;
-  return rh <= Gh && rw <= Gw;
+  if (R < 1) return false;
+  bool found = false;
+  unsigned long long best_hi = 0, best_lo = 1;
+  auto consider = [&](long long h, long long w) {
+    if (h > Gh || w > Gw) return;
+    const unsigned long long a = (unsigned long long)Gh * w, b = (unsigned long long)Gw * h;
+    const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+    const unsigned __int128 l = (unsigned __int128)hi * best_lo, r = (unsigned __int128)best_hi * lo;
+    if (!found || l < r || (l == r && h < rh)) {
+      found = true;
+      best_hi = hi;
+      best_lo = lo;
+      rh = (int)h;
+      rw = (int)w;
+    }
+  };
+  for (long long d = 1; d * d <= R; ++d) {
+    if (R % d) continue;
+    consider(d, R / d);
+    consider(R / d, d);
+  }
+  return found;
 }
 
 // README canvas rules: at or below native the original attention is kept.
@@ -459,6 +477,7 @@ int area_step_info(const area_problem* p, int step, area_step* out) {
   out->max_windows = 4 * wi.ty.n * wi.tx.n;
   out->q_total = wi.q_total;
   out->R = wi.R;
+  if (wi.R > 0) bridge_cells(wi.R, p->Gh, p->Gw, out->bridge_rh, out->bridge_rw);
   return AREA_OK;
 }
 

@@ -1,5 +1,5 @@
 """GPU parity of joint text + image sequences (T > 0): text tokens first, at
-position (0, 0), never pooled, in every key set; text queries dense over all
+position (0, 0), left out of the pooling, in every key set; text queries dense over all
 T + N keys.  Elementwise on the tiny grid with 8 text tokens, sampled rows on
 FLUX.1 2048^2 with 512 text tokens; plans and bridges bit-exact; the
 per-step driver equals the composed calls."""

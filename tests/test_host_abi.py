@@ -233,6 +233,7 @@ def test_schedule_at_pages_knobs_matches_oracle(name):
         st = A.area_step_info(p, wl.p1_steps + t)
         assert st["w"] == w, (name, t)
         assert st["R"] == O.bridge_size(w, 1, 2), (name, t)
+        assert (st["bridge_rh"], st["bridge_rw"]) == O.bridge_cells(st["R"], wl.Gh, wl.Gw), (name, t)
     # configured knobs: fixed bridge at every window step, none on coarse steps
     q = prob(name)
     assert all(A.area_step_info(q, wl.p1_steps + t)["R"] == wl.bridge_k for t in range(wl.p2_steps))
@@ -268,3 +269,32 @@ def test_phase1_steps_for_sigma_matches_oracle():
     assert L.area_phase1_steps_for_sigma(arr, -1, 0.7, ctypes.byref(out)) == -1
     assert L.area_phase1_steps_for_sigma(arr, 2, float("nan"), ctypes.byref(out)) == -1
     assert L.area_phase1_steps_for_sigma(arr, 2, 0.7, None) == -1
+
+
+def test_bridge_cell_grid_matches_oracle():
+    """The library's bridge cell grid (area_step_info) against the oracle's
+    reading, for every workload and for random grids and bridge sizes."""
+    for name in ("tiny-32", "flux-2048", "flux-4096", "flux-6144", "qwen-6144x2048"):
+        wl = W.get(name)
+        st = A.area_step_info(prob(name), wl.p1_steps)
+        assert (st["bridge_rh"], st["bridge_rw"]) == O.bridge_cells(wl.bridge_k, wl.Gh, wl.Gw), name
+    rnd = random.Random(77)
+    checked = 0
+    while checked < 200:
+        Gh, Gw = 2 * rnd.randint(4, 200), 2 * rnd.randint(4, 200)
+        R = rnd.randint(1, 2000)
+        p = A.Problem(B=1, H=1, D=64, Gh=Gh, Gw=Gw, native_h=4, native_w=4, p1_steps=0, p2_steps=1,
+                      w_start=8, w_min=8, halo=1, bridge_k=R)
+        try:
+            ref = O.bridge_cells(R, Gh, Gw)
+        except ValueError:
+            with pytest.raises(A.AreaError):
+                A.area_validate(p)
+            continue
+        try:
+            A.area_validate(p)
+        except A.AreaError:
+            continue  # rejected for another reason (for example a cell row wider than 4096)
+        st = A.area_step_info(p, 0)
+        assert (st["bridge_rh"], st["bridge_rw"]) == ref, (Gh, Gw, R)
+        checked += 1

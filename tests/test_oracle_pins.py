@@ -586,6 +586,62 @@ def test_bridge_selection_brute_force():
         assert len(set(idx.tolist())) == R
 
 
+def test_bridge_cells_golden():
+    """Hand-worked cell grids (tests/golden/bridge_cells.json), including the
+    non-square Qwen grid where the most nearly square cells are 12 x 16
+    tokens, and a bridge size with no fitting grid."""
+    g = gold("bridge_cells.json")
+    for c in g["cases"]:
+        if c["rh"] is None:
+            with pytest.raises(ValueError):
+                O.bridge_cells(c["R"], c["Gh"], c["Gw"])
+            continue
+        assert O.bridge_cells(c["R"], c["Gh"], c["Gw"]) == (c["rh"], c["rw"]), c["note"]
+
+
+def test_bridge_cells_most_square_brute_force():
+    """The cell grid minimises the cells' elongation over every factor pair
+    of R that fits the grid, measured here as |log(cell height / cell
+    width)| with exact fractions (an independent formulation), equal
+    elongations going to the fewest cell rows."""
+    g = rng(23)
+    for _ in range(400):
+        Gh, Gw = int(g.integers(2, 200)), int(g.integers(2, 200))
+        R = int(g.integers(1, 600))
+        pairs = [(a, R // a) for a in range(1, R + 1) if R % a == 0 and a <= Gh and R // a <= Gw]
+        if not pairs:
+            with pytest.raises(ValueError):
+                O.bridge_cells(R, Gh, Gw)
+            continue
+
+        def elong(pr):
+            ratio = Fraction(Gh, pr[0]) / Fraction(Gw, pr[1])
+            return max(ratio, 1 / ratio)
+
+        best = min(elong(pr) for pr in pairs)
+        expect = min(pr for pr in pairs if elong(pr) == best)
+        assert O.bridge_cells(R, Gh, Gw) == expect, (Gh, Gw, R)
+
+
+def test_bridge_cells_partition_the_grid():
+    """Every image token lies in exactly one cell, and cell sides differ by at
+    most one token along each axis."""
+    for (Gh, Gw, R) in [(384, 128, 256), (384, 384, 512), (12, 20, 6), (30, 34, 15)]:
+        rh, rw = O.bridge_cells(R, Gh, Gw)
+        owner = -np.ones((Gh, Gw), dtype=np.int64)
+        hs, ws = set(), set()
+        for a in range(rh):
+            y0, y1 = a * Gh // rh, (a + 1) * Gh // rh
+            hs.add(y1 - y0)
+            for c in range(rw):
+                x0, x1 = c * Gw // rw, (c + 1) * Gw // rw
+                ws.add(x1 - x0)
+                assert (owner[y0:y1, x0:x1] < 0).all()
+                owner[y0:y1, x0:x1] = a * rw + c
+        assert (owner >= 0).all()
+        assert max(hs) - min(hs) <= 1 and max(ws) - min(ws) <= 1
+
+
 def test_bridge_prefers_outliers():
     k = rng(21).standard_normal((16 * 16, 8)) * 0.1
     k[37] += 5.0
@@ -689,7 +745,7 @@ def test_step_phases_counts():
 
 
 # ------------------------------------------------------------ text tokens ----
-# READING R20: T text tokens first, at RoPE position (0, 0), never pooled or windowed,
+# READING R20: T text tokens first, at RoPE position (0, 0), left out of pooling and windowing,
 # keys of every key set; text queries attend densely to all T + N keys.
 
 def _text_inputs(T, Gh, Gw, D=16, seed=0):
@@ -698,7 +754,7 @@ def _text_inputs(T, Gh, Gw, D=16, seed=0):
 
 
 def test_text_phase1_key_count_from_pages():
-    # [summary] Phase I: text tokens are never pooled, so each of the N queries attends to T + N/f^2 keys
+    # [summary] Phase I: text keys skip the pooling, so every image query sees T + N/f^2 keys
     T, Gh, Gw, f = 5, 8, 12, 2
     q, k, v = _text_inputs(T, Gh, Gw)
     kp, vp = O.pool_kv(k, v, Gh, Gw, f, O.POOL_MEAN, 10000.0, T=T)
