@@ -89,8 +89,8 @@ class Schedule:
         self.energy = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.float32, device=dev)
         self.energy_q = torch.empty((p.Gh // 2, p.Gw // 2), dtype=torch.int32, device=dev)
         fs = sorted({st["f"] for st in self.sched if st["phase"] == A.PHASE_COARSE})
-        self.kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev),
-                        torch.empty((B, H, N // (f * f), D), dtype=torch.float16, device=dev)) for f in fs}
+        self.kpv = {f: (torch.empty((B, H, N // (f * f), D), dtype=torch.float32, device=dev),
+                        torch.empty((B, H, N // (f * f), D), dtype=torch.float32, device=dev)) for f in fs}
 
     def bridge(self, s):
         """The step's bridge-index view [B, H, R_s] of the shared buffer (None without a bridge)."""
@@ -329,8 +329,8 @@ def main():
     full_ms = agg["full_call"]
     full_tflops = tflops(sc.full_flops, agg["full_kernel"])
     area_tflops = tflops(coarse_fl + win_fl, area_ms)
-    # pooling bytes (mean mode): read K and V, write pooled K and V
-    pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 2
+    # pooling bytes (mean mode): read K and V (bf16), write pooled K and V (fp32)
+    pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 4
                      for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
     dwt_bytes = n_win * (wl.C * N * 4 + (N // 4) * 8)
 

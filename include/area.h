@@ -29,8 +29,17 @@
  *  * The attention MFMAs take IEEE fp16 operands (rotated Q and K, V and
  *    the probabilities P; three mantissa bits finer than bf16, same rate)
  *    with fp32 accumulation; the library converts keys and values into
- *    workspace and queries in registers as they are loaded.  Entries
- *    of q, k and v must therefore stay below 32768 in magnitude.
+ *    workspace and queries in registers as they are loaded.  Range policy:
+ *    fp16 ends at 65504 while bf16 reaches 3e38, so every 64-key tile of K
+ *    and of V, and every query row, is stored at its own power-of-two scale
+ *    2^-e: e = 0 (the values unchanged) while the block's largest magnitude
+ *    lies in [2^-8, 2^15), otherwise chosen so that it lands in
+ *    [2^13, 2^14).  Work items that meet a nonzero e run a second attention
+ *    kernel that undoes the scales in fp32 (O is kept in the units of the
+ *    largest V scale met so far, so P never exceeds fp16).  Any finite input
+ *    with |q| |k| sqrt(D) < 2^100 and |v| < 2^100 is handled at the
+ *    relative precision of unit-scale data; the bridge's mean key saturates
+ *    keys at 2^28.  Inputs holding inf or NaN give undefined outputs.
  *  * The library never allocates device memory.  Calls that need scratch
  *    take a caller-provided workspace of at least area_workspace_bytes()
  *    bytes (device memory, 256-byte aligned).
@@ -231,13 +240,13 @@ const char* area_last_error(void);
 
 /* Phase I pooling (blog Fase I; ai.info summary Phase I; README Phase I
  * bullet).  k, v: [B][H][T+Gh*Gw][D] bf16, un-rotated.  kp, vp: outputs
- * [B][H][T+(Gh/f)*(Gw/f)][D] in IEEE fp16 (the attention operand type, three
- * mantissa bits finer than bf16).  Block (by, bx) sits at index
- * by*(Gw/f)+bx.
+ * [B][H][T+(Gh/f)*(Gw/f)][D] in fp32 (the pooled means unrounded, and the
+ * inputs' full range kept; area_coarse_attn converts them to its fp16
+ * operands).  Block (by, bx) sits at index by*(Gw/f)+bx.
  * kp = RoPE(pool(k)) at integer coarse position (by, bx); vp = pool(v).
  * pool per p->pool_mode (blog "Cómo entra en tu pipeline": the pooling
  * tunable takes subsample, mean, medoid or random): the mean of the block's
- * f*f tokens (fp32 sum, one rounding), or one token of the block, the same
+ * f*f tokens (fp32 sum, one fp32 division), or one token of the block, the same
  * token for K and V: the block centre (offset (f/2, f/2)); the medoid (the
  * token whose un-rotated key has the smallest sum of Euclidean distances to
  * the block's keys, float64, per pair the squared differences summed over
@@ -253,8 +262,8 @@ int area_pool_kv(const area_problem* p, int f, const void* k, const void* v,
  * full-resolution image query (and the T text keys that area_pool_kv puts
  * first).  q: [B][H][T+Gh*Gw][D] bf16 un-rotated; kp, vp as produced by
  * area_pool_kv; out: [B][H][T+Gh*Gw][D] bf16, image rows written.  Workspace:
- * area_workspace_bytes(p, AREA_OP_COARSE). kp and vp are fp16 as produced by
- * area_pool_kv. */
+ * area_workspace_bytes(p, AREA_OP_COARSE). kp and vp are the fp32 rows
+ * area_pool_kv produces. */
 int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp,
                      const void* vp, void* out, void* ws, size_t ws_bytes, void* stream);
 

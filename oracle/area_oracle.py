@@ -628,19 +628,32 @@ def bridge_cells(R: int, Gh: int, Gw: int) -> Tuple[int, int]:
     return best[2], best[3]
 
 
+K_MEAN_CLAMP = 2.0 ** 28   # keys saturate here inside the mean-key sum only
+BRIDGE_CHUNK = 1024         # rows per exact int64 partial sum
+
+
 def bridge_scores(kbh: np.ndarray) -> np.ndarray:
     """Deviation of every key from the head's global mean key ([summary]
     Phase II: bridge tokens are chosen by their deviation from the global
     mean key).  READING R13: kbh [N, D] un-rotated keys.  The mean is exact:
-    keys in fixed point round_half_even(k * 2^24) summed as integers, then
-    mu_d = sum / (2^24 * N) in one float64 division.  The score is
+    keys (saturated at +-2^28) in fixed point round_half_even(k * 2^24)
+    summed as integers, the sum T rounded once to float64, then
+    mu_d = T / (2^24 * N) in one float64 division.  The score is
     s_j = sum over d ascending of (k_jd - mu_d)^2 in float64 (no fused
     multiply-add)."""
     k = np.asarray(kbh, dtype=np.float64)
     N, D = k.shape
-    kq = np.rint(k * 16777216.0).astype(np.int64)
-    tot = kq.sum(axis=0)                      # exact integer sum
-    mu = tot.astype(np.float64) / (16777216.0 * N)
+    # Keys enter the mean saturated at +-2^28 (so |kq| <= 2^52 and any 1024
+    # rows sum exactly in int64); the total over all rows is an exact
+    # integer T, converted to float64 once (rounded to nearest) as
+    # hi * 2^32 + lo with hi = floor(T / 2^32), both parts exact in float64.
+    kq = np.rint(np.clip(k, -K_MEAN_CLAMP, K_MEAN_CLAMP) * 16777216.0).astype(np.int64)
+    pad = (-N) % BRIDGE_CHUNK
+    chunks = np.concatenate([kq, np.zeros((pad, D), np.int64)]).reshape(-1, BRIDGE_CHUNK, D).sum(axis=1)
+    mu = np.empty(D, dtype=np.float64)
+    for d in range(D):
+        T = sum(int(x) for x in chunks[:, d])  # exact (Python integers)
+        mu[d] = (float(T >> 32) * 4294967296.0 + float(T & 0xFFFFFFFF)) / (16777216.0 * N)
     s = np.zeros(N, dtype=np.float64)
     for d in range(D):
         t = k[:, d] - mu[d]

@@ -287,10 +287,10 @@ def area_pool_kv(p: Problem, f: int, k, v, kp=None, vp=None):
     _need(k, torch.bfloat16, shp, "k")
     _need(v, torch.bfloat16, shp, "v")
     M = p.T + ((p.Gh // f) * (p.Gw // f) if f > 0 else 0)
-    kp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float16, device=k.device) if kp is None else kp
-    vp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float16, device=k.device) if vp is None else vp
-    _need(kp, torch.float16, (p.B, p.H, M, p.D), "kp")
-    _need(vp, torch.float16, (p.B, p.H, M, p.D), "vp")
+    kp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float32, device=k.device) if kp is None else kp
+    vp = torch.empty((p.B, p.H, M, p.D), dtype=torch.float32, device=k.device) if vp is None else vp
+    _need(kp, torch.float32, (p.B, p.H, M, p.D), "kp")
+    _need(vp, torch.float32, (p.B, p.H, M, p.D), "vp")
     s, ref = _pp(p)
     _check(lib().area_pool_kv(ref, f, _ptr(k), _ptr(v), _ptr(kp), _ptr(vp), _stream()))
     return kp, vp
@@ -300,8 +300,8 @@ def area_coarse_attn(p: Problem, f: int, q, kp, vp, out=None, ws=None):
     torch = _torch()
     _need(q, torch.bfloat16, (p.B, p.H, p.L, p.D), "q")
     M = p.T + ((p.Gh // f) * (p.Gw // f) if f > 0 else 0)
-    _need(kp, torch.float16, (p.B, p.H, M, p.D), "kp")
-    _need(vp, torch.float16, (p.B, p.H, M, p.D), "vp")
+    _need(kp, torch.float32, (p.B, p.H, M, p.D), "kp")
+    _need(vp, torch.float32, (p.B, p.H, M, p.D), "vp")
     out = torch.empty_like(q) if out is None else out
     _need(out, torch.bfloat16, (p.B, p.H, p.L, p.D), "out")
     ws = workspace(p, OP_COARSE, q.device) if ws is None else ws

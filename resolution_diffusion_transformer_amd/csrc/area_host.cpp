@@ -297,6 +297,35 @@ static int64_t N_of(const area_problem& p) { return (int64_t)p.Gh * p.Gw; }
 static int64_t L_of(const area_problem& p) { return (int64_t)p.T + N_of(p); }  // rows per sequence
 static size_t tok_bytes(const area_problem& p) { return (size_t)BH_of(p) * L_of(p) * p.D * 2; }
 
+// Regions of the dense-attention workspace (full attention, the text pass
+// and coarse attention; M = T + Gh*Gw key rows per (batch, head) covers
+// every pooling factor down to f = 1): fp16 key rows, fp16 V^T tiles, the
+// (cos, sin) tables, per-tile exponents of K and V, per-(batch, head) range
+// flags.
+struct DenseLayout {
+  size_t kr, vt, tab, kexp, vexp, flags, total;
+};
+
+static DenseLayout dense_layout(const area_problem& p) {
+  const int64_t BH = BH_of(p);
+  const int M = (int)L_of(p);
+  DenseLayout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  l.kr = take(tok_bytes(p));
+  l.vt = take(vt_bytes(BH, M, p.D));
+  l.tab = take(rope_table_bytes(p.Gh, p.Gw, p.D));
+  l.kexp = take(tile_exp_bytes(BH, M));
+  l.vexp = take(tile_exp_bytes(BH, M));
+  l.flags = take(range_words(BH, BH * (((int64_t)M + kAttnBM - 1) / kAttnBM)) * sizeof(int));
+  l.total = off;
+  return l;
+}
+
 struct WindowMax {
   int64_t q_total = 0, max_items = 0, max_gtiles = 0;
   int max_windows = 0, n_base = 0, max_R = 0;
@@ -320,7 +349,7 @@ static WindowMax window_max(const area_problem& p) {
 
 // Regions of the windowed-attention workspace, in order.
 struct WindowLayout {
-  size_t rope, slots, items, kg, vg, blist, bcount, total;
+  size_t rope, slots, items, kg, vg, blist, bcount, kexp, vexp, flags, total;
 };
 
 static WindowLayout window_layout(const area_problem& p) {
@@ -340,6 +369,9 @@ static WindowLayout window_layout(const area_problem& p) {
   l.vg = take((size_t)BH * m.max_gtiles * kAttnBN * p.D * 2);
   l.blist = take((size_t)m.max_windows * BH * std::max(m.max_R, 1) * 4);
   l.bcount = take((size_t)m.max_windows * BH * 4);
+  l.kexp = take((size_t)BH * m.max_gtiles * sizeof(int));
+  l.vexp = take((size_t)BH * m.max_gtiles * sizeof(int));
+  l.flags = take(range_words(BH, BH * m.max_items) * sizeof(int));
   l.total = off;
   return l;
 }
@@ -371,7 +403,7 @@ static StepLayout step_layout(const area_problem& p) {
       int f = ramp_factor(p, f0, s);
       M = std::max(M, N / ((size_t)f * f));
     }
-    const size_t pooled = align_up(BH * (M + p.T) * p.D * 2);
+    const size_t pooled = align_up(BH * (M + p.T) * p.D * 4);  // fp32 pooled rows
     l.kp = 0;
     l.vp = pooled;
     l.coarse_ws = 2 * pooled;
@@ -402,11 +434,9 @@ static size_t workspace_bytes(const area_problem& p, int op) {
   switch (op) {
     case AREA_OP_STEP:
       return step_layout(p).total;
-    case AREA_OP_FULL:  // rotated K, V^T tiles, (cos, sin) table
-      return align_up(tok_bytes(p)) + align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D)) +
-             align_up(rope_table_bytes(p.Gh, p.Gw, p.D));
-    case AREA_OP_COARSE:  // V^T tiles of the pooled values, (cos, sin) table
-      return align_up(vt_bytes(BH_of(p), (int)L_of(p), p.D)) + align_up(rope_table_bytes(p.Gh, p.Gw, p.D));
+    case AREA_OP_FULL:    // key rows, V^T tiles, (cos, sin) tables, tile exponents, flags
+    case AREA_OP_COARSE:  // the same for the pooled keys and values
+      return dense_layout(p).total;
     case AREA_OP_PLAN: {
       if (canvas_gated(p) || p.p2_steps == 0) return 0;
       WindowMax m = window_max(p);
@@ -431,6 +461,26 @@ static int check_ws(const area_problem& p, int op, void* ws, size_t ws_bytes) {
                                       std::to_string(need));
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(AREA_E_WORKSPACE, "workspace must be 256-byte aligned");
   return AREA_OK;
+}
+
+// Dense attention of query rows q0 .. q0 + Nq - 1 over every key of the
+// sequences (text and image, RoPE at native positions; text at (0, 0)) in a
+// workspace of dense_layout: full attention (all rows) and the text pass
+// (the T text rows).
+static int dense_pass(const area_problem& p, char* b, const void* q, const void* k, const void* v, void* out, int q0,
+                      int Nq, void* stream) {
+  const int64_t BH = BH_of(p);
+  const int L = (int)L_of(p);
+  const DenseLayout l = dense_layout(p);
+  int* kexp = (int*)(b + l.kexp);
+  int* vexp = (int*)(b + l.vexp);
+  int* flags = (int*)(b + l.flags);
+  int rc = launch_rope_table(b + l.tab, p.Gh, p.Gw, p.D, p.rope_theta, 1.0f, flags, BH + 1, stream);
+  if (rc) return rc;
+  rc = launch_kv_tiles(k, v, b + l.tab, b + l.kr, b + l.vt, kexp, vexp, flags, BH, L, p.D, false, p.T, p.Gw, stream);
+  if (rc) return rc;
+  return launch_dense_attn(q, b + l.tab, p.T, p.Gh, p.Gw, b + l.kr, b + l.vt, kexp, vexp, flags, out, BH, Nq, q0, L,
+                           L, p.D, stream);
 }
 
 }  // namespace area
@@ -567,17 +617,22 @@ int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp
   if (f < 1 || p->Gh % f || p->Gw % f) return fail(AREA_E_SHAPE, pstr("f must divide both grid sides, f", f));
   rc = check_ws(*p, AREA_OP_COARSE, ws, ws_bytes);
   if (rc) return rc;
-  int64_t BH = BH_of(*p);
-  int N = (int)N_of(*p);
-  int M = N / (f * f);
-  char* vt = (char*)ws;
-  char* tab = vt + align_up(vt_bytes(BH, (int)L_of(*p), p->D));
+  const int64_t BH = BH_of(*p);
+  const int N = (int)N_of(*p);
+  const int M = p->T + N / (f * f);  // text rows, then the pooled grid
+  const DenseLayout l = dense_layout(*p);
+  char* b = (char*)ws;
+  int* kexp = (int*)(b + l.kexp);
+  int* vexp = (int*)(b + l.vexp);
+  int* flags = (int*)(b + l.flags);
   // queries turn at coarse-grid positions (row / f, column / f), as the keys
-  rc = launch_rope_table(tab, p->Gh, p->Gw, p->D, p->rope_theta, (float)f, stream);
+  rc = launch_rope_table(b + l.tab, p->Gh, p->Gw, p->D, p->rope_theta, (float)f, flags, BH + 1, stream);
   if (rc) return rc;
-  rc = launch_vt(vp, vt, BH, p->T + M, p->D, false, stream);
+  rc = launch_kv_tiles(kp, vp, b + l.tab, b + l.kr, b + l.vt, kexp, vexp, flags, BH, M, p->D, true, p->T, p->Gw,
+                       stream);
   if (rc) return rc;
-  return launch_dense_attn(q, tab, p->T, p->Gh, p->Gw, kp, vt, out, BH, N, p->T, p->T + N, p->T + M, p->D, stream);
+  return launch_dense_attn(q, b + l.tab, p->T, p->Gh, p->Gw, b + l.kr, b + l.vt, kexp, vexp, flags, out, BH, N, p->T,
+                           p->T + N, M, p->D, stream);
 }
 
 int area_full_attn(const area_problem* p, const void* q, const void* k, const void* v, void* out,
@@ -587,42 +642,14 @@ int area_full_attn(const area_problem* p, const void* q, const void* k, const vo
   if (!q || !k || !v || !out) return fail(AREA_E_INVALID, "NULL tensor");
   rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
   if (rc) return rc;
-  int64_t BH = BH_of(*p);
-  const int L = (int)L_of(*p);
-  char* kr = (char*)ws;
-  char* vt = kr + align_up(tok_bytes(*p));
-  char* tab = vt + align_up(vt_bytes(BH, L, p->D));
-  rc = launch_rope_table(tab, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
-  if (rc) return rc;
-  rc = launch_prep(k, kr, tab, BH, p->T, p->Gh, p->Gw, p->D, stream);
-  if (rc) return rc;
-  rc = launch_vt(v, vt, BH, L, p->D, true, stream);
-  if (rc) return rc;
-  return launch_dense_attn(q, tab, p->T, p->Gh, p->Gw, kr, vt, out, BH, L, 0, L, L, p->D, stream);
+  return dense_pass(*p, (char*)ws, q, k, v, out, 0, (int)L_of(*p), stream);
 }
 
 }  // extern "C"
 
 namespace area {
 
-// The T text queries against every key (text and image), in a workspace of
-// the full-attention layout: rotated fp16 K, V^T tiles, (cos, sin) table.
-// Text queries sit at position (0, 0), so they are not turned.
-static int text_pass(const area_problem& p, char* ws, const void* q, const void* k, const void* v, void* out,
-                     void* stream) {
-  const int64_t BH = BH_of(p);
-  const int L = (int)L_of(p);
-  char* kr = ws;
-  char* vt = kr + align_up(tok_bytes(p));
-  char* tab = vt + align_up(vt_bytes(BH, L, p.D));
-  int rc = launch_rope_table(tab, p.Gh, p.Gw, p.D, p.rope_theta, 1.0f, stream);
-  if (rc) return rc;
-  rc = launch_prep(k, kr, tab, BH, p.T, p.Gh, p.Gw, p.D, stream);
-  if (rc) return rc;
-  rc = launch_vt(v, vt, BH, L, p.D, true, stream);
-  if (rc) return rc;
-  return launch_dense_attn(q, tab, p.T, p.Gh, p.Gw, kr, vt, out, BH, p.T, 0, L, L, p.D, stream);
-}
+
 
 }  // namespace area
 
@@ -636,7 +663,7 @@ int area_text_attn(const area_problem* p, const void* q, const void* k, const vo
   if (p->T == 0) return AREA_OK;
   rc = check_ws(*p, AREA_OP_FULL, ws, ws_bytes);
   if (rc) return rc;
-  return text_pass(*p, (char*)ws, q, k, v, out, stream);
+  return dense_pass(*p, (char*)ws, q, k, v, out, 0, p->T, stream);
 }
 
 int area_dwt_detail(const area_problem* p, int C, const float* latent, float* energy,
@@ -731,7 +758,10 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   w.vg = base + l.vg;
   w.blist = (int*)(base + l.blist);
   w.bcount = (int*)(base + l.bcount);
-  rc = launch_rope_table(base + l.rope, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, stream);
+  w.kexp = (int*)(base + l.kexp);
+  w.vexp = (int*)(base + l.vexp);
+  w.flags = (int*)(base + l.flags);
+  rc = launch_rope_table(base + l.rope, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, w.flags, BH_of(*p) + 1, stream);
   if (rc) return rc;
   return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, q, k, v, base + l.rope, out, w, stream);
 }
@@ -775,7 +805,7 @@ int area_attn_step(const area_problem* p, int step, int C, const float* latent, 
       rc = area_window_attn(p, step, plan, wsum, bridge, q, k, v, out, base + l.window_ws,
                             ws_bytes - l.window_ws, stream);
       if (rc || p->T == 0) return rc;
-      return text_pass(*p, base + l.window_ws, q, k, v, out, stream);
+      return dense_pass(*p, base + l.window_ws, q, k, v, out, 0, p->T, stream);
     }
   }
 }

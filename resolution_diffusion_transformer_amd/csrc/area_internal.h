@@ -85,17 +85,15 @@ int measure_mfma_peak(void* sink, double* tflops, void* stream);
 // have been validated by the caller.
 typedef void* stream_t;
 
-// fp16 keys for dense attention: xo = RoPE(x) at grid positions through
-// the first table of launch_rope_table (built with div 1).  Sequences are T
-// text tokens (position (0, 0), not rotated) then the Gh x Gw image grid.
-int launch_prep(const void* x, void* xo, const void* tab, int64_t BH, int T, int Gh, int Gw, int D, stream_t s);
 // (cos, sin) tables of every axis position p < P = max(Gh, Gw) and
 // frequency k < D/4 at angle (p / div) * theta^(-4k/D), fp32: first
-// [P][D/4] float2 (the windowed gather turns keys through it), then
+// [P][D/4] float2 (the key conversions turn keys through it), then
 // [D/8][P] float4 of frequency pairs (the attention kernels turn queries
-// through it).
+// through it).  The same launch clears the n_flags words at `flags` (the
+// per-(batch, head) range flags of the call's key and value tiles).
 size_t rope_table_bytes(int Gh, int Gw, int D);
-int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, stream_t s);
+int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, int* flags, int64_t n_flags,
+                      stream_t s);
 int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, int T, int Gh, int Gw,
                 int D, int f, int mode, unsigned long long seed, float theta, stream_t s);
 int launch_dwt(const float* latent, float* energy, int32_t* energy_q, int C, int Gh, int Gw,
@@ -118,19 +116,32 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int T, int Gh, int Gw
 constexpr int kBridgeSortMax = 4096;  // cells per row of the bridge cell grid
 size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
 
-// fp16 V^T tiles of 64 keys: vt[bh][t][d][k] = v[bh][64 t + k][d], zero
-// padded; v is bf16 (bf16_in) or fp16.
+// Dense key/value operands, one 64-key tile per work-group: fp16 key rows
+// kr[bh][M][D] and fp16 V^T tiles vt[bh][t][d][k] = v[bh][64 t + k][d]
+// (zero padded), each tile scaled by its own power of two 2^-e with e in
+// kexp / vexp[bh][t] (0 for magnitudes in [2^-8, 2^15)); flags[bh] is set
+// when a tile of (b, h) has a nonzero exponent.  k and v are [BH][M][D]:
+// bf16 sequences (T text rows, then the Gh x Gw grid; keys turned by RoPE
+// through the first table of launch_rope_table) or, with f32_in, fp32 pooled
+// rows whose keys are already turned.
 size_t vt_bytes(int64_t BH, int M, int D);
-int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, stream_t s);
+size_t tile_exp_bytes(int64_t BH, int M);  // one int32 per (batch*head, 64-key tile)
+int launch_kv_tiles(const void* k, const void* v, const void* rope, void* kr, void* vt, int* kexp, int* vexp,
+                    int* flags, int64_t BH, int M, int D, bool f32_in, int T, int Gw, stream_t s);
 
 // Attention of bf16 queries (turned by RoPE through the tables `rope` of
 // launch_rope_table as they are loaded; rows below q_text are text, row
-// q_text + n is image token n of the Gh x Gw grid) over fp16 rotated key
-// rows and V^T tiles, bf16 output.  Queries are rows q0 .. q0 + Nq - 1 of sequences of q_rows rows (q
-// and out share that layout); keys are the Nk rows of k_rot / vt per
-// (batch, head).
+// q_text + n is image token n of the Gh x Gw grid) over the key rows and
+// V^T tiles of launch_kv_tiles, bf16 output.  Queries are rows q0 .. q0 +
+// Nq - 1 of sequences of q_rows rows (q and out share that layout); keys are
+// the Nk rows of k_rot / vt per (batch, head).
 int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int Gw, const void* k_rot,
-                      const void* vt, void* out, int64_t BH, int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
+                      const void* vt, const int* kexp, const int* vexp, int* flags, void* out, int64_t BH,
+                      int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
+// Words of the range region of an attention call: BH flags, then the count
+// and list of work items the scaled attention kernel runs (cleared, flags and
+// count, by the call's rope-table launch).
+inline size_t range_words(int64_t BH, int64_t work) { return (size_t)BH + 1 + (size_t)work; }
 
 struct WindowAttnArgs {
   int Gh, Gw, D, R;
@@ -150,6 +161,9 @@ struct WindowWs {
   void* vg;        // [BH][max_gtiles][D][64] fp16 gathered V^T tiles
   int* blist;      // [max_windows][BH][R] kept bridge tokens
   int* bcount;     // [max_windows][BH]
+  int* kexp;       // [BH][max_gtiles] power-of-two exponent of each gathered key tile
+  int* vexp;       // [BH][max_gtiles] the same for the V^T tiles
+  int* flags;      // range_words(BH, BH * max_items): flags set by the gather, then the scaled items
 };
 // q, k, v: un-rotated bf16 sequences; the gather turns the keys and the
 // attention kernel the queries by RoPE through the tables `rope` of

@@ -51,6 +51,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 #include "area_internal.h"
 
@@ -82,63 +83,184 @@ __device__ inline u16 f2bf(float f) {
   return (u16)(u >> 16);
 }
 
-__device__ inline u16 bf_to_f16(u16 b) {
-  _Float16 h = (_Float16)__uint_as_float(((unsigned)b) << 16);
-  return __builtin_bit_cast(u16, h);
-}
-
 // Two-axis RoPE of one 16-byte chunk (8 bf16 channels, 4 rotation pairs)
 // into fp16: c01, c23 hold the chunk's four (cos, sin) pairs, interleaved.
-// Pair (a, b) becomes (a cos - b sin, a sin + b cos) times `scale`, rounded
-// to nearest.
-__device__ inline u32x4 rope8_f16(const u32x4 raw, const float4 c01, const float4 c23, const float scale = 1.0f) {
+// Pair (a, b) becomes (a cos - b sin, a sin + b cos) times `scale`; the
+// largest magnitude of these values is folded into `mx`, and with e != 0
+// they are further scaled by 2^-e before rounding to nearest.
+__device__ inline u32x4 rope8_f16_max(const u32x4 raw, const float4 c01, const float4 c23, const float scale,
+                                      float& mx, const int e = 0) {
   const float co[4] = {c01.x, c01.z, c23.x, c23.z};
   const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float a = __uint_as_float(raw[j] << 16), b = __uint_as_float(raw[j] & 0xFFFF0000u);
-    const _Float16 x0 = (_Float16)((a * co[j] - b * sn[j]) * scale);
-    const _Float16 x1 = (_Float16)((a * sn[j] + b * co[j]) * scale);
+    float y0 = (a * co[j] - b * sn[j]) * scale;
+    float y1 = (a * sn[j] + b * co[j]) * scale;
+    mx = fmaxf(mx, fmaxf(fabsf(y0), fabsf(y1)));
+    if (e != 0) {
+      y0 = ldexpf(y0, -e);
+      y1 = ldexpf(y1, -e);
+    }
+    const _Float16 x0 = (_Float16)y0, x1 = (_Float16)y1;
     r[j] = (unsigned)__builtin_bit_cast(u16, x0) | ((unsigned)__builtin_bit_cast(u16, x1) << 16);
   }
   return r;
 }
 
-// ------------------------------------------------------------ V^T tiles --
-// out[bh][t][d][k] = in[bh][64 t + k][d] as fp16, zero for rows >= M.
-template <int D, bool IN_BF16>
-__global__ __launch_bounds__(256) void vt_kernel(const u16* __restrict__ in, u16* __restrict__ out, int M,
-                                                 int tiles) {
-  constexpr int CPR = D / 8;
+// ------------------------------------------------------- operand range --
+// fp16 holds magnitudes up to 65504 (normal down to 2^-14), less than bf16
+// inputs can reach.  Every 64-key tile of K (and of V) is therefore stored
+// as x * 2^-e with its own power-of-two exponent e, and every query row
+// likewise: e = 0 while the block's largest magnitude m lies in
+// [2^-8, 2^15) (or m is 0, subnormal, infinite or NaN), otherwise
+// m * 2^-e lands in [2^13, 2^14).  Power-of-two scaling is exact, so
+// in-range data is stored exactly as before; the attention kernel undoes
+// nonzero exponents in fp32 (see its "scaled" loop).
+__device__ inline int operand_exponent(float m) {
+  const int eb = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m) for normal m
+  if (eb == 128 || eb == -127) return 0;
+  return (eb >= 15 || eb < -8) ? eb - 13 : 0;
+}
+
+// Largest magnitude over the 256 threads of a work-group (non-negative
+// inputs; `red` holds 4 floats).
+__device__ inline float block_max4(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float maxabs8(const float* x, float m) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) m = fmaxf(m, fmaxf(fabsf(x[i]), fabsf(x[i + 1])));
+  return m;
+}
+
+__device__ inline void bf8_to_f32(const u32x4 raw, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(raw[i] << 16);
+    x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+  }
+}
+
+// x * 2^-e rounded to fp16 (to nearest even), 8 values into 16 bytes.
+__device__ inline u32x4 f16x8_scaled(const float* x, int e) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 a = (_Float16)ldexpf(x[2 * i], -e), b = (_Float16)ldexpf(x[2 * i + 1], -e);
+    r[i] = (unsigned)__builtin_bit_cast(u16, a) | ((unsigned)__builtin_bit_cast(u16, b) << 16);
+  }
+  return r;
+}
+
+// Two-axis RoPE of 8 channels in fp32: pair (a, b) -> (a cos - b sin,
+// a sin + b cos) with the chunk's four (cos, sin) pairs from the [P][D/4]
+// table row `cs`.
+__device__ inline void rope8_f32(float* x, const float4* cs) {
+  const float4 c01 = cs[0], c23 = cs[1];
+  const float co[4] = {c01.x, c01.z, c23.x, c23.z};
+  const float sn[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = x[2 * j], b = x[2 * j + 1];
+    x[2 * j] = a * co[j] - b * sn[j];
+    x[2 * j + 1] = a * sn[j] + b * co[j];
+  }
+}
+
+// ------------------------------------------------- dense K rows, V^T tiles --
+// One work-group per (64-key tile t, batch*head): rows 64 t .. 64 t + 63 of
+// the key and value sequences ([BH][M][D], bf16 or fp32).  bf16 keys are
+// turned by RoPE at their grid position (rows below T are text at (0, 0),
+// row T + n is image token n) through the [P][D/4] (cos, sin) table `rope`;
+// fp32 keys (pooled, already turned) are taken as they are.  Outputs:
+// fp16 key rows kr[bh][row][D] (rows < M only) and the fp16 V^T tile
+// vt[bh][t][d][k] = v[bh][64 t + k][d] (zero past M), each scaled by the
+// tile's own power of two (kexp, vexp[bh][t]; flags[bh] set when nonzero).
+template <int D, bool F32_IN>
+__global__ __launch_bounds__(256) void kv_tiles_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                       const float* __restrict__ rope, u16* __restrict__ kr,
+                                                       u16* __restrict__ vt, int* __restrict__ kexp,
+                                                       int* __restrict__ vexp, int* __restrict__ flags, int M,
+                                                       int tiles, int T, int Gw) {
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int HALF = CPR / 2;   // chunks per axis half
+  constexpr int NF = D / 4;       // frequencies per axis half
+  constexpr int CH = BN * CPR / 256;
   constexpr int LS = D + 8;
   __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
+  __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t bh = blockIdx.y;
-  const u16* src = in + bh * (int64_t)M * D;
-  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
-    int row = c / CPR, col = c - row * CPR;
-    int key = t * BN + row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < M) {
-      v = *reinterpret_cast<const u32x4*>(src + (int64_t)key * D + col * 8);
-      if constexpr (IN_BF16) {
+  float kx[CH][8], vx[CH][8];
+  float mk = 0.0f, mv = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = (unsigned)bf_to_f16((u16)(v[i] & 0xFFFFu)) | ((unsigned)bf_to_f16((u16)(v[i] >> 16)) << 16);
+  for (int i = 0; i < CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / CPR, col = c - row * CPR;
+    const int key = t * BN + row;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kx[i][e] = vx[i][e] = 0.0f;
+    if (key < M) {
+      const int64_t off = (bh * (int64_t)M + key) * D + col * 8;
+      if constexpr (F32_IN) {
+        const float4* kp = reinterpret_cast<const float4*>((const float*)k + off);
+        const float4* vp = reinterpret_cast<const float4*>((const float*)v + off);
+        const float4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+        const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kx[i][e] = kk[e];
+          vx[i][e] = vv[e];
+        }
+      } else {
+        bf8_to_f32(*reinterpret_cast<const u32x4*>((const u16*)k + off), kx[i]);
+        bf8_to_f32(*reinterpret_cast<const u32x4*>((const u16*)v + off), vx[i]);
+        int py = 0, px = 0;
+        if (key >= T) {
+          py = (key - T) / Gw;
+          px = key - T - py * Gw;
+        }
+        // chunk col: channels 8 col .. 8 col + 7, pairs 4 (col % HALF) .. of its axis half
+        rope8_f32(kx[i], reinterpret_cast<const float4*>(rope + 2 * ((col < HALF ? py : px) * NF + 4 * (col % HALF))));
       }
     }
-    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = v;
+    mk = maxabs8(kx[i], mk);
+    mv = maxabs8(vx[i], mv);
+  }
+  const int ek = operand_exponent(block_max4(mk, red));
+  const int ev = operand_exponent(block_max4(mv, red));
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / CPR, col = c - row * CPR;
+    const int key = t * BN + row;
+    if (key < M) *reinterpret_cast<u32x4*>(kr + (bh * (int64_t)M + key) * D + col * 8) = f16x8_scaled(kx[i], ek);
+    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = f16x8_scaled(vx[i], ev);
+  }
+  if (threadIdx.x == 0) {
+    kexp[bh * tiles + t] = ek;
+    vexp[bh * tiles + t] = ev;
+    if (ek | ev) flags[bh] = 1;
   }
   __syncthreads();
-  u16* dst = out + (bh * tiles + t) * (int64_t)D * BN;
+  u16* dst = vt + (bh * tiles + t) * (int64_t)D * BN;
   for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
     int d = c / (BN / 8), k8 = c - d * (BN / 8);
-    u32x4 v;
+    u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      v[i] = (unsigned)buf[(8 * k8 + 2 * i) * LS + d] | ((unsigned)buf[(8 * k8 + 2 * i + 1) * LS + d] << 16);
-    *reinterpret_cast<u32x4*>(dst + d * BN + 8 * k8) = v;
+      o[i] = (unsigned)buf[(8 * k8 + 2 * i) * LS + d] | ((unsigned)buf[(8 * k8 + 2 * i + 1) * LS + d] << 16);
+    *reinterpret_cast<u32x4*>(dst + d * BN + 8 * k8) = o;
   }
 }
 
@@ -270,23 +392,27 @@ __global__ __launch_bounds__(256) void bridge_compact_kernel(const int32_t* __re
 // then the T text tokens, then zero rows.  Sequences hold the T text rows
 // first, image token n at row T + n.  K rows are turned by RoPE at their
 // token's grid position (text rows at (0, 0), unturned) through the (cos,
-// sin) table `rope` and written as fp16; V rows are converted bf16 -> fp16
-// and written transposed.
+// sin) table `rope`; V rows are written transposed.  Both are fp16, scaled by
+// the tile's own power of two (kexp, vexp[bh][tile]; flags[bh] set when
+// nonzero), as kv_tiles_kernel does for dense key sets.
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ plan, const int* __restrict__ gtiles,
                                                      const int* __restrict__ n_items, const int* __restrict__ kv_tile_off,
                                                      const int* __restrict__ list, const int* __restrict__ count,
                                                      const u16* __restrict__ k, const u16* __restrict__ v,
                                                      const float* __restrict__ rope, u16* __restrict__ kg,
-                                                     u16* __restrict__ vg, int64_t cap_tiles, int R, int Tt, int Gw,
+                                                     u16* __restrict__ vg, int* __restrict__ kexp, int* __restrict__ vexp,
+                                                     int* __restrict__ flags, int64_t cap_tiles, int R, int Tt, int Gw,
                                                      int N, int64_t BH) {
   constexpr int CPR = D / 8;
   constexpr int HALF = CPR / 2;  // chunks per axis half
   constexpr int NF = D / 4;      // frequencies per axis half
+  constexpr int CH = BN * CPR / 256;
   constexpr int LS = D + 8;
   __shared__ __attribute__((aligned(16))) u16 buf[BN * LS];
   __shared__ int s_tok[BN];
   __shared__ int s_py[BN], s_px[BN];
+  __shared__ float red[4];
   const int g = blockIdx.x;
   const int64_t bh = blockIdx.y;
   if (g >= n_items[1]) return;
@@ -321,23 +447,39 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   const u16* ksrc = k + bh * (int64_t)(Tt + N) * D;
   const u16* vsrc = v + bh * (int64_t)(Tt + N) * D;
   u16* kdst = kg + (bh * cap_tiles + T) * (int64_t)BN * D;
-  for (int c = threadIdx.x; c < BN * CPR; c += 256) {
-    int row = c / CPR, col = c - row * CPR;
-    int tok = s_tok[row];
-    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+  float kx[CH][8], vx[CH][8];
+  float mk = 0.0f, mv = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / CPR, col = c - row * CPR;
+    const int tok = s_tok[row];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kx[i][e] = vx[i][e] = 0.0f;
     if (tok >= 0) {
       // chunk col: channels 8 col .. 8 col + 7, rotation pairs 4 (col % HALF) ..
       // of the row (first half) or column (second half) axis
       const int pos = col < HALF ? s_py[row] : s_px[row];
-      const float4* cs = reinterpret_cast<const float4*>(rope + 2 * (pos * NF + 4 * (col % HALF)));
-      kv = rope8_f16(*reinterpret_cast<const u32x4*>(ksrc + (int64_t)tok * D + col * 8), cs[0], cs[1]);
-      vv = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)tok * D + col * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vv[i] = (unsigned)bf_to_f16((u16)(vv[i] & 0xFFFFu)) | ((unsigned)bf_to_f16((u16)(vv[i] >> 16)) << 16);
+      bf8_to_f32(*reinterpret_cast<const u32x4*>(ksrc + (int64_t)tok * D + col * 8), kx[i]);
+      bf8_to_f32(*reinterpret_cast<const u32x4*>(vsrc + (int64_t)tok * D + col * 8), vx[i]);
+      rope8_f32(kx[i], reinterpret_cast<const float4*>(rope + 2 * (pos * NF + 4 * (col % HALF))));
     }
-    *reinterpret_cast<u32x4*>(kdst + row * D + col * 8) = kv;
-    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = vv;
+    mk = maxabs8(kx[i], mk);
+    mv = maxabs8(vx[i], mv);
+  }
+  const int ek = operand_exponent(block_max4(mk, red));
+  const int ev = operand_exponent(block_max4(mv, red));
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / CPR, col = c - row * CPR;
+    *reinterpret_cast<u32x4*>(kdst + row * D + col * 8) = f16x8_scaled(kx[i], ek);
+    *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = f16x8_scaled(vx[i], ev);
+  }
+  if (threadIdx.x == 0) {
+    kexp[bh * cap_tiles + T] = ek;
+    vexp[bh * cap_tiles + T] = ev;
+    if (ek | ev) flags[bh] = 1;
   }
   __syncthreads();
   u16* vdst = vg + (bh * cap_tiles + T) * (int64_t)D * BN;
@@ -364,6 +506,10 @@ struct AttnArgs {
   int Nq;              // dense mode: queries per head, rows q0 .. q0 + Nq - 1
   int q0, q_rows;      // first query row (window mode: image token n is row q0 + n); rows per head
   int64_t k_rows, k_tiles;  // per-(batch*head) strides of k and vt
+  const int* kexp;     // [BH][k_tiles] power-of-two exponent of each key tile (stored K * 2^-e)
+  const int* vexp;     // [BH][k_tiles] the same for the V^T tiles
+  const int* flags;    // [BH] nonzero: some tile of the (batch, head) has a nonzero exponent
+  int* redo;           // [0]: count, then the logical ids of the items the scaled kernel runs
   int n_kv;            // dense mode: keys per query
   int n_qtiles;        // dense mode: query tiles per head
   int grid;            // launched work-groups (multiple of 8)
@@ -556,7 +702,9 @@ __device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage
 // Scores are in log2 units relative to the running maximum m: the queries
 // carry log2(e)/sqrt(D), and the first MFMA of each accumulator starts from
 // nm = -m instead of zero, so no per-score scale or subtraction is left.
-template <int D, int QG>
+// With ZERO_START (the scaled loop) the accumulators start from zero and the
+// caller shifts and rescales the raw scores itself.
+template <int D, int QG, bool ZERO_START = false>
 __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2], const u16* ks, int n, int hi,
                                                               const f16x8 (&qf)[QG][D / 16],
                                                               const f32x16 (&sc)[QG][2], const f32x16 (&nm)[QG],
@@ -579,8 +727,14 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
     if (j + PF < NT) fr[j % PF] = lds_frag(ks, k_frag_off<D>(j + PF, n, hi));
     else vfr[j + PF - NT] = lds_frag(vt, vt_frag_off<D>(j + PF - NT, n, hi));
 #pragma unroll
-    for (int g = 0; g < QG; ++g)
-      sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
+    for (int g = 0; g < QG; ++g) {
+      if constexpr (ZERO_START) {
+        const f32x16 zero = {};
+        sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? zero : sn[g][j & 1], 0, 0, 0);
+      } else {
+        sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
+      }
+    }
     // P of EPM scores, converted in pairs (one packed conversion per pair)
 #pragma unroll
     for (int e = EPM * j; e < EPM * j + EPM; e += 2) {
@@ -641,30 +795,23 @@ __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D 
 // else one.
 constexpr int kAttnGroupsPerCu = kAttnQG == 1 && kAttnWaves == 4 ? 2 : 1;
 
-template <int D, bool WIN>
-__global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const AttnArgs a) {
+// One work item (256 queries of one (batch, head): a query tile of the
+// dense sequence, or of one window record) over its whole key set.  SCALED
+// selects the loop that undoes nonzero operand exponents; the plain loop
+// hands such an item to the scaled kernel through the list a.redo.
+template <int D, bool WIN, bool SCALED>
+__device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const int64_t L, u16* ks0,
+                                                                u16* vt0, u16* ks1, u16* vt1) {
   constexpr int QG = kAttnQG;     // 32-query groups per wave
   constexpr int BM = kAttnBM;     // kAttnWaves waves x QG groups x 32 queries
   constexpr int KD = D / 16;
   constexpr int DB = D / 32;
-  constexpr int K_ELEMS = BN * D;
-  constexpr int V_ELEMS = D * BN;
   static_assert(BM == kAttnWaves * 32 * QG, "query tile");
-
-  // two LDS stages, as separate objects so that the compiler can tell a DMA
-  // into one stage from reads of the other
-  __shared__ __attribute__((aligned(16))) u16 ks0[K_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 vt0[V_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 ks1[K_ELEMS];
-  __shared__ __attribute__((aligned(16))) u16 vt1[V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hi = lane >> 5;
 
-  // ---- work item (XCD-aware order: logical ids are contiguous per XCD)
-  const int pid = blockIdx.x;
-  const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
   int64_t bh;
   int qtile = 0, rec = 0;
   int qy0 = 0, qx0 = 0, qh = 0, qw = 1;
@@ -736,6 +883,9 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     }
   }
   f16x8 qf[QG][KD];
+  int eq[QG];         // per query row: operands carry q * log2(e)/sqrt(D) * 2^-eq
+  int ev_cur = 0;     // V^T unit: O holds O_true * 2^-ev_cur (scaled loop)
+  float lsc = 1.0f;   // 2^-d of the tile whose P is turned next (scaled loop)
 
   const int nt = (nkv + BN - 1) / BN;
   const float c = a.c;
@@ -763,9 +913,16 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   kbase = uniform_ptr(kbase);
   vtbase = uniform_ptr(vtbase);
   nkv = __builtin_amdgcn_readfirstlane(nkv);
-  auto step = [&](f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn, const u16* vtc, int j,
-                  u16* kdma, int ktile, u16* vdma, int vtile)
+  // The scaled variant (SC) handles nonzero exponents: its score
+  // accumulators start from zero, so a tile's raw scores are
+  // s * 2^-(eq + ek); after phase B they are moved to s - m in fp32 for the
+  // next step.  A V^T tile stored at 2^-ev adds ev - ev_cur to its scores
+  // (P carries 2^(ev - ev_cur)), and a tile with ev above ev_cur first moves
+  // O to the new unit, so P never grows; l stays in true units.
+  auto step = [&](auto scaled_tag, f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn,
+                  const u16* vtc, int j, u16* kdma, int ktile, u16* vdma, int vtile)
       __attribute__((always_inline)) {
+    constexpr bool SC = decltype(scaled_tag)::value;
     // phase A's first K fragments, read ahead of the tile DMAs so their LDS
     // latency overlaps them
     f16x8 kfr[kFragAhead];
@@ -779,7 +936,7 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     f16x8 pf[QG][4];
     f16x8 vfr[kFragAhead];
     float psum[QG];
-    phase_a<D, QG>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr, psum);
+    phase_a<D, QG, SC>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr, psum);
     // keep P's computation in this block: its only use is after the branch
 #pragma unroll
     for (int g = 0; g < QG; ++g)
@@ -812,8 +969,10 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           nm[g][i] -= dlt;
-          snext[g][0][i] -= dlt;
-          snext[g][1][i] -= dlt;
+          if constexpr (!SC) {  // raw scores of the scaled loop take the new m at their fix-up
+            snext[g][0][i] -= dlt;
+            snext[g][1][i] -= dlt;
+          }
         }
         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
         const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
@@ -832,8 +991,39 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     const int valid = nkv - (j + 1) * BN;
     if (valid < BN) mask_tail<QG>(snext, valid, hi);
     phase_b<D, QG>(o, vtc, n, hi, pf, vfr);
+    if constexpr (SC) {
 #pragma unroll
-    for (int g = 0; g < QG; ++g) l_run[g] += psum[g];
+      for (int g = 0; g < QG; ++g) l_run[g] += psum[g] * lsc;
+      if (j + 1 < nt) {
+        const int64_t eb = bh * a.k_tiles + t0 + j + 1;
+        const int ek = a.kexp[eb], ev = a.vexp[eb];
+        int d = ev - ev_cur;
+        if (d > 0) {
+          const float al = ldexpf(1.0f, -d);
+#pragma unroll
+          for (int g = 0; g < QG; ++g)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) o[g][db][i] *= al;
+          ev_cur = ev;
+          d = 0;
+        }
+        lsc = ldexpf(1.0f, -d);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+          const float sc = ldexpf(1.0f, eq[g] + ek);
+          const float cc = nm[g][0] + (float)d;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) snext[g][kb][i] = fmaf(snext[g][kb][i], sc, cc);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < QG; ++g) l_run[g] += psum[g];
+    }
   };
 
   // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each step
@@ -847,14 +1037,56 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   issue_v<D>(vt0, 0, tid, wave_u, vtbase);
   issue_k<D>(ks1, min(1, nt - 1), tid, wave_u, nkv, kbase);
   __builtin_amdgcn_sched_barrier(0);  // all three DMAs before the rotation's waits
+  // Each query row carries its own power-of-two exponent eq (operand_exponent
+  // of the row's largest turned and scaled magnitude, the two lanes of a
+  // query column agreeing); a row with eq != 0 is converted again at
+  // 2^-eq.
+  bool any_eq = false;
 #pragma unroll
-  for (int g = 0; g < QG; ++g)
+  for (int g = 0; g < QG; ++g) {
+    float mx = 0.0f;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c));
+      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16_max(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c, mx));
+    eq[g] = operand_exponent(pair_max(qvalid[g] ? mx : 0.0f));
+    if (eq[g] != 0) {
+      any_eq = true;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+        qf[g][kd] =
+            __builtin_bit_cast(f16x8, rope8_f16_max(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c, mx, eq[g]));
+    }
+  }
+  // An item runs the scaled loop when a query row or a key or value tile of
+  // its (batch, head) carries a nonzero exponent; the plain kernel lists
+  // such an item for the scaled kernel and ends once its DMAs have landed.
+  constexpr bool scaled = SCALED;
+  if constexpr (!SCALED) {
+    if (__syncthreads_or(any_eq ? 1 : 0) || a.flags[bh] != 0) {
+      if (tid == 0) a.redo[1 + atomicAdd(a.redo, 1)] = (int)L;
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      return;
+    }
+  }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  tile_scores<D, QG>(sa, ks0, n, hi, qf);
+  if constexpr (scaled) {
+    tile_scores<D, QG>(sa, ks0, n, hi, qf);
+    // raw scores are s * 2^-(eq + ek); the first tile also fixes the V unit
+    const int64_t eb = bh * a.k_tiles + t0;
+    const int ek0 = a.kexp[eb];
+    ev_cur = a.vexp[eb];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      const float sc = ldexpf(1.0f, eq[g] + ek0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[g][kb][i] *= sc;
+    }
+  } else {
+    tile_scores<D, QG>(sa, ks0, n, hi, qf);
+  }
   if (nkv < BN) mask_tail<QG>(sa, nkv, hi);
   // the first tile sets the running maximum (every query has a key there)
 #pragma unroll
@@ -877,14 +1109,26 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
 #pragma unroll
   for (int g = 0; g < QG; ++g) any_q |= qvalid[g];
   if (__any(any_q)) {
-    for (int j = 0; j < nt; j += 2) {
-      step(sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
-      if (j + 1 >= nt) break;
-      step(sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();
+    if constexpr (!scaled) {
+      for (int j = 0; j < nt; j += 2) {
+        step(std::false_type{}, sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (j + 1 >= nt) break;
+        step(std::false_type{}, sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+      }
+    } else {
+      for (int j = 0; j < nt; j += 2) {
+        step(std::true_type{}, sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (j + 1 >= nt) break;
+        step(std::true_type{}, sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+      }
     }
   } else {
     // none of this wave's queries is in the item (the last, partial query
@@ -903,7 +1147,7 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     float lt = pair_sum(l_run[g]);
-    float inv = 1.0f / lt;
+    float inv = ldexpf(1.0f / lt, ev_cur);
     if (!qvalid[g]) continue;
     // an opaque copy of the query's row: its addresses are recomputed here
     // rather than kept live in registers across the key loop
@@ -941,6 +1185,36 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
           *reinterpret_cast<float4*>(srow + d) = v4;
         }
     }
+  }
+}
+
+// The plain kernel: one work item per work-group, logical ids contiguous
+// per XCD (consecutive items share a window's keys in one L2).
+template <int D, bool WIN>
+__global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const AttnArgs a) {
+  // two LDS stages, as separate objects so that the compiler can tell a DMA
+  // into one stage from reads of the other
+  __shared__ __attribute__((aligned(16))) u16 ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 vt0[D * BN];
+  __shared__ __attribute__((aligned(16))) u16 ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 vt1[D * BN];
+  const int pid = blockIdx.x;
+  const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
+  attn_item<D, WIN, false>(a, L, ks0, vt0, ks1, vt1);
+}
+
+// The scaled kernel: work-groups walk the items the plain kernel listed
+// (none for operands within fp16's comfortable range, so it ends at once).
+template <int D, bool WIN>
+__global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_scaled_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 ks0[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 vt0[D * BN];
+  __shared__ __attribute__((aligned(16))) u16 ks1[BN * D];
+  __shared__ __attribute__((aligned(16))) u16 vt1[D * BN];
+  const int cnt = a.redo[0];
+  for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
+    attn_item<D, WIN, true>(a, a.redo[1 + i], ks0, vt0, ks1, vt1);
+    __syncthreads();
   }
 }
 
@@ -1039,15 +1313,20 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
   if (g > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "attention grid too large");
   b.grid = (int)g;
   dim3 grid((unsigned)b.grid);
+  // the scaled kernel's work-groups walk the listed items (one per CU fits)
+  dim3 grid_scaled((unsigned)std::min<int64_t>(g, 1024));
   AttnEvents ev = attn_events();
   if (ev.begin) {
     hipError_t e = hipEventRecord((hipEvent_t)ev.begin, st);
     if (e != hipSuccess) return fail(AREA_E_HIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
   }
-  if (D == 128)
+  if (D == 128) {
     hipLaunchKernelGGL((attn_kernel<128, WIN>), grid, dim3(kThreads), 0, st, b);
-  else
+    hipLaunchKernelGGL((attn_scaled_kernel<128, WIN>), grid_scaled, dim3(kThreads), 0, st, b);
+  } else {
     hipLaunchKernelGGL((attn_kernel<64, WIN>), grid, dim3(kThreads), 0, st, b);
+    hipLaunchKernelGGL((attn_scaled_kernel<64, WIN>), grid_scaled, dim3(kThreads), 0, st, b);
+  }
   int rc = check_launch(WIN ? "attn_kernel<window>" : "attn_kernel<dense>");
   if (rc) return rc;
   if (ev.end) {
@@ -1061,23 +1340,37 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
 
 size_t vt_bytes(int64_t BH, int M, int D) { return (size_t)BH * ((M + BN - 1) / BN) * BN * D * 2; }
 
-int launch_vt(const void* v, void* vt, int64_t BH, int M, int D, bool bf16_in, stream_t s) {
+size_t tile_exp_bytes(int64_t BH, int M) { return (size_t)BH * ((M + BN - 1) / BN) * sizeof(int); }
+
+int launch_kv_tiles(const void* k, const void* v, const void* rope, void* kr, void* vt, int* kexp, int* vexp,
+                    int* flags, int64_t BH, int M, int D, bool f32_in, int T, int Gw, stream_t s) {
   if (BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
-  int tiles = (M + BN - 1) / BN;
+  const int tiles = (M + BN - 1) / BN;
+  if (tiles == 0) return AREA_OK;
   dim3 grid((unsigned)tiles, (unsigned)BH);
   hipStream_t st = (hipStream_t)s;
+  const float* tab = (const float*)rope;
   if (D == 128) {
-    if (bf16_in) hipLaunchKernelGGL((vt_kernel<128, true>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
-    else hipLaunchKernelGGL((vt_kernel<128, false>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+    if (f32_in)
+      hipLaunchKernelGGL((kv_tiles_kernel<128, true>), grid, dim3(256), 0, st, k, v, tab, (u16*)kr, (u16*)vt, kexp,
+                         vexp, flags, M, tiles, T, Gw);
+    else
+      hipLaunchKernelGGL((kv_tiles_kernel<128, false>), grid, dim3(256), 0, st, k, v, tab, (u16*)kr, (u16*)vt, kexp,
+                         vexp, flags, M, tiles, T, Gw);
   } else {
-    if (bf16_in) hipLaunchKernelGGL((vt_kernel<64, true>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
-    else hipLaunchKernelGGL((vt_kernel<64, false>), grid, dim3(256), 0, st, (const u16*)v, (u16*)vt, M, tiles);
+    if (f32_in)
+      hipLaunchKernelGGL((kv_tiles_kernel<64, true>), grid, dim3(256), 0, st, k, v, tab, (u16*)kr, (u16*)vt, kexp,
+                         vexp, flags, M, tiles, T, Gw);
+    else
+      hipLaunchKernelGGL((kv_tiles_kernel<64, false>), grid, dim3(256), 0, st, k, v, tab, (u16*)kr, (u16*)vt, kexp,
+                         vexp, flags, M, tiles, T, Gw);
   }
-  return check_launch("vt_kernel");
+  return check_launch("kv_tiles_kernel");
 }
 
 int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int Gw, const void* k_rot,
-                      const void* vt, void* out, int64_t BH, int Nq, int q0, int q_rows, int Nk, int D, stream_t s) {
+                      const void* vt, const int* kexp, const int* vexp, int* flags, void* out, int64_t BH,
+                      int Nq, int q0, int q_rows, int Nk, int D, stream_t s) {
   AttnArgs a = {};
   a.q = (const u16*)q;
   a.rope_P = std::max(Gh, Gw);
@@ -1093,6 +1386,10 @@ int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int G
   a.q_rows = q_rows;
   a.k_rows = Nk;
   a.k_tiles = (Nk + BN - 1) / BN;
+  a.kexp = kexp;
+  a.vexp = vexp;
+  a.flags = flags;
+  a.redo = flags + BH;
   a.n_kv = Nk;
   a.n_qtiles = (Nq + kAttnBM - 1) / kAttnBM;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
@@ -1129,13 +1426,13 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   if (w.D == 128)
     hipLaunchKernelGGL((gather_kernel<128>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
                        (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k,
-                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N,
-                       w.BH);
+                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, ws.kexp, ws.vexp, ws.flags,
+                       w.max_gtiles, R, w.T, w.Gw, N, w.BH);
   else
     hipLaunchKernelGGL((gather_kernel<64>), gg, dim3(256), 0, st, plan, (const int*)iw.gtiles, (const int*)iw.n_items,
                        (const int*)iw.kv_tile_off, (const int*)ws.blist, (const int*)ws.bcount, (const u16*)k,
-                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, w.max_gtiles, R, w.T, w.Gw, N,
-                       w.BH);
+                       (const u16*)v, (const float*)rope, (u16*)ws.kg, (u16*)ws.vg, ws.kexp, ws.vexp, ws.flags,
+                       w.max_gtiles, R, w.T, w.Gw, N, w.BH);
   rc = check_launch("gather_kernel");
   if (rc) return rc;
   AttnArgs a = {};
@@ -1153,6 +1450,10 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   a.T = w.T;
   a.k_rows = w.max_gtiles * BN;
   a.k_tiles = w.max_gtiles;
+  a.kexp = ws.kexp;
+  a.vexp = ws.vexp;
+  a.flags = ws.flags;
+  a.redo = ws.flags + w.BH;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)w.D));
   a.plan = plan;
   a.wsum = wsum;

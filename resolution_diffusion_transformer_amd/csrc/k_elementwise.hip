@@ -26,15 +26,7 @@ InvFreq make_inv_freq(int D, float theta) {
   return f;
 }
 
-__device__ inline float bf16_to_f32(unsigned short h) { return __uint_as_float(((unsigned)h) << 16); }
-
-// float -> bfloat16, round to nearest even (inputs are finite).
-__device__ inline unsigned short f32_to_bf16(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
-
+// 8 bf16 channels (16 bytes) to fp32 (exact).
 __device__ inline void unpack8(const uint4& r, float* x) {
   const unsigned w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -44,24 +36,10 @@ __device__ inline void unpack8(const uint4& r, float* x) {
   }
 }
 
-// float -> IEEE half, round to nearest even.
-__device__ inline unsigned short f32_to_f16(float f) {
-  _Float16 h = (_Float16)f;
-  return __builtin_bit_cast(unsigned short, h);
-}
-
-__device__ inline uint4 pack8_f16(const float* x) {
-  unsigned w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (unsigned)f32_to_f16(x[2 * i]) | ((unsigned)f32_to_f16(x[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-__device__ inline uint4 pack8(const float* x) {
-  unsigned w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (unsigned)f32_to_bf16(x[2 * i]) | ((unsigned)f32_to_bf16(x[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// 8 channels as fp32 into the two float4 of chunk i of a row-major fp32 buffer.
+__device__ inline void store8_f32(float4* dst, int64_t i, const float* x) {
+  dst[2 * i] = make_float4(x[0], x[1], x[2], x[3]);
+  dst[2 * i + 1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
 // k-th output of the SplitMix64 generator (Steele, Lea and Flood, OOPSLA
@@ -111,45 +89,6 @@ __device__ inline void rope_apply(float* x, const Rot4& r) {
   }
 }
 
-// Key preparation for dense attention, one thread per 8 channels of a
-// token of the joint sequence (T text tokens, then the image grid):
-// xo = RoPE(x) at the token's grid position (text tokens at (0, 0), not
-// rotated), written as IEEE fp16 (the MFMA operand type of the attention
-// kernels; bf16 -> fp16 is exact in fp16's normal range and the rotated
-// values keep three more mantissa bits than bf16 would).  The (cos, sin)
-// come from the [P][D/4] table of rope_table_kernel.
-template <int D>
-__global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ x_in, uint4* __restrict__ xo,
-                                                   const float2* __restrict__ tab, int64_t BH, int L, int T,
-                                                   int Gw) {
-  constexpr int CPT = D / 8;     // 16-byte chunks per row
-  constexpr int HALF = CPT / 2;  // chunks per axis half
-  constexpr int NF = D / 4;      // frequencies per axis half
-  const int64_t total = BH * (int64_t)L * CPT;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i % CPT);
-    const int row = (int)((i / CPT) % L);
-    int py = 0, px = 0;
-    if (row >= T) {
-      const int n = row - T;
-      py = n / Gw;
-      px = n - py * Gw;
-    }
-    // chunk c: channels 8c .. 8c+7, pairs 4 (c % HALF) .. + 3 of its axis half
-    const float2* cs = tab + (c < HALF ? py : px) * NF + 4 * (c % HALF);
-    Rot4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r.co[j] = cs[j].x;
-      r.sn[j] = cs[j].y;
-    }
-    float x[8];
-    unpack8(x_in[i], x);
-    rope_apply(x, r);
-    xo[i] = pack8_f16(x);
-  }
-}
-
 // (cos, sin) of every (axis position, frequency) pair the attention kernels
 // rotate by, c_k(p) = sincos((p / div) * inv_freq[k]) for p < P, k < D/4, in
 // two layouts: tab[p][k] (float2; a thread's chunk of one token reads
@@ -158,9 +97,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint4* __restrict__ x_i
 // positions read neighbouring entries, the attention kernels' query load).
 // Angles are formed as rope_cs forms those of the pooled keys: the fp32
 // position times the fp32 inverse frequency, then sincosf.
+// The same launch clears the call's n_flags range-flag words (grid-strided).
 __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, float2* __restrict__ tabq, int P,
-                                                         int NF, float div, InvFreq f) {
+                                                         int NF, float div, InvFreq f, int* __restrict__ flags,
+                                                         int64_t n_flags) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = e; i < n_flags; i += (int64_t)gridDim.x * blockDim.x) flags[i] = 0;
   if (e >= P * NF) return;
   const int p = e / NF, k = e - p * NF;
   const float pos = (float)p / div;
@@ -177,12 +119,13 @@ __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ ta
 // random mode the token at its seeded offset (medoid mode has a kernel of its
 // own below).  Keys are then rotated at the coarse position (by, bx); values
 // are not rotated.
-// One rounding at the end, to fp16 (the attention MFMA operand type).
+// The pooled rows are written in fp32 (the f*f sum and the division in fp32,
+// no further rounding).
 // Grid: x over the (output row, chunk) pairs of one (batch, head), y over
 // (batch, head), both grid-strided.
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                                   uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
+                                                   float4* __restrict__ kp, float4* __restrict__ vp, int64_t BH,
                                                    int Gh, int Gw, int f, int mode, int T, unsigned long long seed,
                                                    InvFreq fr) {
   constexpr int CPT = D / 8;
@@ -199,8 +142,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, 
       if (r < T) {
         unpack8(k[(bh * L + r) * CPT + c], ks);
         unpack8(v[(bh * L + r) * CPT + c], vs);
-        kp[i] = pack8_f16(ks);
-        vp[i] = pack8_f16(vs);
+        store8_f32(kp, i, ks);
+        store8_f32(vp, i, vs);
         continue;
       }
       const int np = (int)(r - T);
@@ -236,8 +179,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, 
         }
       }
       rope_apply(ks, rope_cs(c, D, (float)by, (float)bx, fr));
-      kp[i] = pack8_f16(ks);
-      vp[i] = pack8_f16(vs);
+      store8_f32(kp, i, ks);
+      store8_f32(vp, i, vs);
     }
   }
 }
@@ -251,10 +194,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint4* __restrict__ k, 
 // token ascending; ties go to the smaller row-major offset.  Lanes take the
 // candidates in turn and a wave reduction picks the winner; then the row is
 // written like the other modes: K rotated at the coarse position (by, bx),
-// V unrotated, both fp16.
+// V unrotated, both fp32.
 template <int D>
 __global__ __launch_bounds__(64) void pool_medoid_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
-                                                         uint4* __restrict__ kp, uint4* __restrict__ vp, int64_t BH,
+                                                         float4* __restrict__ kp, float4* __restrict__ vp, int64_t BH,
                                                          int Gh, int Gw, int f, int T, InvFreq fr) {
 #pragma clang fp contract(off)
   constexpr int CPT = D / 8;
@@ -312,17 +255,17 @@ __global__ __launch_bounds__(64) void pool_medoid_kernel(const uint4* __restrict
       }
       src = tok(best_j);
     }
-    uint4* ko = kp + (bh * rows_out + r) * CPT;
-    uint4* vo = vp + (bh * rows_out + r) * CPT;
+    float4* ko = kp + (bh * rows_out + r) * (2 * CPT);
+    float4* vo = vp + (bh * rows_out + r) * (2 * CPT);
     for (int c = lane; c < 2 * CPT; c += 64) {
       float x[8];
       if (c < CPT) {
         unpack8(kb[src * CPT + c], x);
         if (r >= T) rope_apply(x, rope_cs(c, D, (float)by, (float)bx, fr));
-        ko[c] = pack8_f16(x);
+        store8_f32(ko, c, x);
       } else {
         unpack8(vb[src * CPT + (c - CPT)], x);
-        vo[c - CPT] = pack8_f16(x);
+        store8_f32(vo, c - CPT, x);
       }
     }
   }
@@ -386,25 +329,14 @@ static dim3 grid_2d(int64_t per_bh, int64_t BH) {
   return dim3((unsigned)gx, (unsigned)gy);
 }
 
-int launch_prep(const void* x, void* xo, const void* tab, int64_t BH, int T, int Gh, int Gw, int D, stream_t s) {
-  const int64_t total = BH * ((int64_t)T + (int64_t)Gh * Gw) * (D / 8);
-  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 1 << 20);
-  if (D == 128)
-    hipLaunchKernelGGL((prep_kernel<128>), dim3(blocks), dim3(256), 0, (hipStream_t)s, (const uint4*)x, (uint4*)xo,
-                       (const float2*)tab, BH, T + Gh * Gw, T, Gw);
-  else
-    hipLaunchKernelGGL((prep_kernel<64>), dim3(blocks), dim3(256), 0, (hipStream_t)s, (const uint4*)x, (uint4*)xo,
-                       (const float2*)tab, BH, T + Gh * Gw, T, Gw);
-  return check_launch("prep_kernel");
-}
-
 size_t rope_table_bytes(int Gh, int Gw, int D) { return 2 * (size_t)std::max(Gh, Gw) * (D / 4) * sizeof(float2); }
 
-int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, stream_t s) {
+int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, int* flags, int64_t n_flags,
+                      stream_t s) {
   const int P = std::max(Gh, Gw), NF = D / 4;
   float2* t = (float2*)tab;
-  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for((int64_t)P * NF)), dim3(256), 0, (hipStream_t)s, t,
-                     t + (size_t)P * NF, P, NF, div, make_inv_freq(D, theta));
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(std::max<int64_t>((int64_t)P * NF, n_flags))), dim3(256), 0,
+                     (hipStream_t)s, t, t + (size_t)P * NF, P, NF, div, make_inv_freq(D, theta), flags, n_flags);
   return check_launch("rope_table_kernel");
 }
 
@@ -417,19 +349,19 @@ int launch_pool(const void* k, const void* v, void* kp, void* vp, int64_t BH, in
     const dim3 grid((unsigned)rows_out, (unsigned)std::min<int64_t>(BH, 65535));
     if (D == 128)
       hipLaunchKernelGGL((pool_medoid_kernel<128>), grid, dim3(64), 0, (hipStream_t)s, (const uint4*)k,
-                         (const uint4*)v, (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, T, fr);
+                         (const uint4*)v, (float4*)kp, (float4*)vp, BH, Gh, Gw, f, T, fr);
     else
       hipLaunchKernelGGL((pool_medoid_kernel<64>), grid, dim3(64), 0, (hipStream_t)s, (const uint4*)k,
-                         (const uint4*)v, (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, T, fr);
+                         (const uint4*)v, (float4*)kp, (float4*)vp, BH, Gh, Gw, f, T, fr);
     return check_launch("pool_medoid_kernel");
   }
   const dim3 grid = grid_2d(rows_out * (D / 8), BH);
   if (D == 128)
     hipLaunchKernelGGL((pool_kernel<128>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
-                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
+                       (float4*)kp, (float4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
   else
     hipLaunchKernelGGL((pool_kernel<64>), grid, dim3(256), 0, (hipStream_t)s, (const uint4*)k, (const uint4*)v,
-                       (uint4*)kp, (uint4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
+                       (float4*)kp, (float4*)vp, BH, Gh, Gw, f, mode, T, seed, fr);
   return check_launch("pool_kernel");
 }
 

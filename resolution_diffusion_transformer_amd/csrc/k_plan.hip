@@ -208,10 +208,6 @@ __global__ __launch_bounds__(256) void plan_wsum_kernel(PlanArgs a, const int* _
   }
 }
 
-__global__ void zero_ints_kernel(int* p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
-
 // ---------------------------------------------------------------- bridge --
 // Workspace: partial fixed-point key sums [BH][chunks][D] int64, the mean
 // key [BH][D] float64, per-cell winners [BH][R] int32.
@@ -222,6 +218,9 @@ struct BridgeWs {
 };
 
 int n_chunks(int N) { return (N + kBridgeChunk - 1) / kBridgeChunk; }
+
+// Keys saturate at this magnitude inside the mean-key sum only.
+constexpr double kMeanClamp = 268435456.0;  // 2^28
 
 BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
   BridgeWs b;
@@ -235,8 +234,9 @@ BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
 }
 
 // Fixed-point sums round_half_even(k * 2^24) over one chunk of rows for
-// every channel.  Thread t reads 8 channels (16 bytes) of a row; 16
-// consecutive threads cover one 128-channel row.
+// every channel, keys saturated at +-2^28 (|term| <= 2^52, so a chunk of
+// 1024 rows sums exactly in int64).  Thread t reads 8 channels (16 bytes) of
+// a row; 16 consecutive threads cover one 128-channel row.
 template <int D>
 __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict__ k, long long* __restrict__ part,
                                                          int N, int T) {
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict
     const unsigned u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      double lo = (double)__uint_as_float(u[i] << 16);
-      double hi = (double)__uint_as_float(u[i] & 0xFFFF0000u);
+      double lo = fmin(fmax((double)__uint_as_float(u[i] << 16), -kMeanClamp), kMeanClamp);
+      double hi = fmin(fmax((double)__uint_as_float(u[i] & 0xFFFF0000u), -kMeanClamp), kMeanClamp);
       acc[2 * i] += (long long)rint(lo * 16777216.0);
       acc[2 * i + 1] += (long long)rint(hi * 16777216.0);
     }
@@ -270,14 +270,18 @@ __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict
   }
 }
 
-// mean_d = (sum of fixed-point keys) / (2^24 N), one float64 division.
+// mean_d = T / (2^24 N): T, the sum of the fixed-point keys, exact in 128
+// bits, rounded once to float64 as hi * 2^32 + lo (hi = floor(T / 2^32) and
+// lo = T mod 2^32 are exact doubles), then one float64 division.
 __global__ void bridge_mean_kernel(const long long* __restrict__ part, double* __restrict__ mean, int nch, int N,
                                    int D) {
   int64_t bh = blockIdx.x;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    long long s = 0;
+    __int128 s = 0;
     for (int c = 0; c < nch; ++c) s += part[((int64_t)bh * nch + c) * D + d];
-    mean[bh * D + d] = (double)s / (16777216.0 * (double)N);
+    const long long hi = (long long)(s >> 32);
+    const unsigned lo = (unsigned)(s & 0xFFFFFFFF);
+    mean[bh * D + d] = ((double)hi * 4294967296.0 + (double)lo) / (16777216.0 * (double)N);
   }
 }
 

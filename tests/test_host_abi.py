@@ -121,9 +121,16 @@ def test_gated_canvas_keeps_full_attention():
     for s in range(12):
         assert A.area_step_info(p, s)["phase"] == A.PHASE_FULL
     assert A.area_workspace_bytes(p, A.OP_WINDOW) == 0
-    # rotated K and V^T tiles (N is a multiple of 64), then the two layouts
-    # of the (cos, sin) table of 64 positions x D/4 frequencies
-    assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * p.B * p.H * p.N * p.D * 2 + 2 * 64 * (p.D // 4) * 8
+    # fp16 key rows and V^T tiles (N is a multiple of 64), the two layouts of
+    # the (cos, sin) table of 64 positions x D/4 frequencies, one exponent per
+    # (head, 64-key tile) for K and for V, and the range words (a flag per
+    # head, the scaled-item count and list of up to N/256 items per head),
+    # each region rounded up to 256 bytes
+    up = lambda x: (x + 255) // 256 * 256
+    BH, tiles = p.B * p.H, p.N // 64
+    expect = (2 * BH * p.N * p.D * 2 + 2 * 64 * (p.D // 4) * 8 + 2 * up(BH * tiles * 4)
+              + up((BH + 1 + BH * (p.N // 256)) * 4))
+    assert A.area_workspace_bytes(p, A.OP_FULL) == expect
 
 
 @pytest.mark.parametrize("over,status", [
@@ -177,10 +184,16 @@ def test_device_calls_reject_bad_arguments_before_launch():
 
 def test_workspace_sizes():
     p = prob("flux-6144")
-    tok = p.B * p.H * p.N * p.D * 2
+    up = lambda x: (x + 255) // 256 * 256
+    BH = p.B * p.H
+    tok = BH * p.N * p.D * 2
     tab = 2 * max(p.Gh, p.Gw) * (p.D // 4) * 8                 # (cos, sin) tables
-    assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * tok + tab  # rotated k + V^T tiles
-    assert A.area_workspace_bytes(p, A.OP_COARSE) == tok + tab    # V^T tiles
+    exps = 2 * up(BH * (p.N // 64) * 4)                        # per-tile exponents of K and V
+    words = up((BH + 1 + BH * (p.N // 256)) * 4)               # range flags, scaled-item list
+    # fp16 key rows + V^T tiles + tables + exponents + range words; coarse
+    # attention has the same layout (pooled keys down to f = 1)
+    assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * tok + tab + exps + words
+    assert A.area_workspace_bytes(p, A.OP_COARSE) == A.area_workspace_bytes(p, A.OP_FULL)
     # window workspace covers the table, gathered k and V^T tiles, and the fp32
     # outputs of the largest step
     wl = W.get("flux-6144")

@@ -566,6 +566,31 @@ def test_bridge_mean_is_exact():
     assert s[0] == acc
 
 
+def test_bridge_mean_saturates_and_stays_exact_beyond_int64():
+    """Keys enter the mean saturated at +-2^28: 40000 equal keys of 2^40 (a
+    fixed-point total of 40000 * 2^52 > 2^63) have the exact mean 2^28, so
+    every score is (2^40 - 2^28)^2 summed over channels; for mixed magnitudes
+    the mean is the exact integer total of the saturated fixed-point keys,
+    rounded once to float64 (Python's correctly rounded int -> float),
+    divided by 2^24 N."""
+    N, D = 40000, 4
+    k = np.full((N, D), 2.0 ** 40)
+    s = O.bridge_scores(k)
+    assert (s == D * (2.0 ** 40 - 2.0 ** 28) ** 2).all()
+    g = rng(24)
+    k = W.bf16_round((g.standard_normal((3000, D)) * 10.0 ** g.integers(-7, 12, (3000, D))).astype(np.float32))
+    k = k.astype(np.float64)
+    kq = np.rint(np.clip(k, -2.0 ** 28, 2.0 ** 28) * 2 ** 24).astype(np.int64)
+    s = O.bridge_scores(k)
+    for j in (0, 17, 2999):
+        acc = 0.0
+        for d in range(D):
+            mu = float(sum(int(x) for x in kq[:, d])) / (2.0 ** 24 * 3000)
+            t = k[j, d] - mu
+            acc = acc + t * t
+        assert s[j] == acc
+
+
 def test_bridge_selection_brute_force():
     g = rng(20)
     for (Gh, Gw, R) in [(16, 16, 16), (12, 20, 6), (32, 32, 16), (24, 8, 8)]:
