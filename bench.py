@@ -242,6 +242,126 @@ def tflops(fl, ms):
     return fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
 
 
+# every configured workload besides the headline one is measured in the same
+# run, with fewer timed passes
+OTHER_CONFIGS = ["tiny-32", "flux-2048", "flux-4096", "qwen-6144x2048"]
+
+
+def measure(A, W, wl, dev, ev, steps, warmup, calibrate=False):
+    """Time `steps` passes of the workload's whole schedule (plus one full
+    attention call each) after `warmup` passes; returns (schedule, metrics)."""
+    import torch
+    p = A.problem_for(wl)
+    log(f"[bench] generating {wl.name} inputs on the GPU")
+    q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
+    lat = torch.from_numpy(W.make_latent(wl)).to(dev)
+    out = torch.empty_like(q)
+    sc = Schedule(A, wl, p, q, k, v, lat, out, ev)
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: counting algorithmic work")
+    flops = sc.count()
+    sched, n_steps = sc.sched, sc.n_steps
+    if calibrate:
+        # one elementwise kernel with a unique name: reads 512 MiB, writes 512 MiB
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log("[bench] calibration kernel (bitwise_not): 512 MiB read, 512 MiB written")
+        del src, dst
+    log(f"[bench] {wl.name}: warmup x{warmup}")
+    for _ in range(warmup):
+        sc.one_pass([])
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: timing x{steps}")
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sc.one_pass(recs)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    agg, per_step, area_ms = sc.summarize(recs, steps)
+    BH, N, D = wl.B * wl.H, wl.N, wl.D
+    n_coarse = sum(1 for st in sched if st["phase"] == A.PHASE_COARSE)
+    n_win = n_steps - n_coarse
+    coarse_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_COARSE)
+    win_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_WINDOW)
+    full_ms = agg["full_call"]
+    # pooling bytes (mean mode): read K and V (bf16), write pooled K and V (fp32)
+    pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 4
+                     for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
+    dwt_bytes = n_win * (wl.C * N * 4 + (N // 4) * 8)
+    p1_ms = agg["pool"] + agg["coarse_call"]
+    p2_ms = agg["dwt"] + agg["plan"] + agg["window_call"]
+    m = {
+        "area_ms_per_step": area_ms / n_steps,
+        "wall_ms_per_pass": wall_ms,
+        "full_ms": full_ms,
+        "full_tflops": tflops(sc.full_flops, agg["full_kernel"]),
+        "area_tflops": tflops(coarse_fl + win_fl, area_ms),
+        "phases": {
+            "phase1_ms_per_step": p1_ms / max(n_coarse, 1),
+            "phase2_ms_per_step": p2_ms / max(n_win, 1),
+            "pool_ms_per_call": agg["pool"] / max(n_coarse, 1),
+            "coarse_ms_per_call": agg["coarse_call"] / max(n_coarse, 1),
+            "coarse_kernel_tflops": tflops(coarse_fl, agg["coarse_kernel"]),
+            "dwt_ms_per_call": agg["dwt"] / max(n_win, 1),
+            "plan_ms_per_call": agg["plan"] / max(n_win, 1),
+            "window_ms_per_call": agg["window_call"] / max(n_win, 1),
+            "window_kernel_tflops": tflops(win_fl, agg["window_kernel"]),
+            "window_kernel_avg_ms": agg["window_kernel"] / max(n_win, 1),
+            "phase1_tflops": tflops(coarse_fl, p1_ms),
+            "phase2_tflops": tflops(win_fl, p2_ms),
+            "pool_gbs": pool_bytes / (agg["pool"] * 1e-3) / 1e9 if agg["pool"] > 0 else 0.0,
+            "dwt_gbs": dwt_bytes / (agg["dwt"] * 1e-3) / 1e9 if agg["dwt"] > 0 else 0.0,
+            # per-phase speedups: full attention over one Phase I step (pool + coarse) and over
+            # one Phase II step (DWT map + plan + windowed attention), averaged over each phase
+            "speedup_phase1": full_ms * n_coarse / p1_ms if p1_ms > 0 else None,
+            "speedup_phase2": full_ms * n_win / p2_ms if p2_ms > 0 else None,
+            "per_step_ms": [round(sum(per_step[s]) / len(per_step[s]), 3) for s in sorted(per_step)],
+            "per_step": sc.step_detail,
+            "schedule_tflop": (coarse_fl + win_fl) / 1e12,
+        },
+        "n_coarse": n_coarse, "n_win": n_win, "steps": steps, "warmup": warmup,
+        "tensors": (p, q, k, v, lat), "flops": flops,
+    }
+    return sc, m
+
+
+def rounded(d):
+    return {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in d.items()}
+
+
+def config_summary(wl, m, cpu):
+    """The per-config record of the bench line: per-phase ms/step, TFLOP/s and
+    fractions of the bf16 MFMA peak, speedups over full attention, and the
+    oracle's time on the host."""
+    ph = m["phases"]
+    return {
+        "grid": [wl.Gh, wl.Gw], "heads": wl.H, "head_dim": wl.D, "steps": m["steps"],
+        "coarse_steps": m["n_coarse"], "window_steps": m["n_win"],
+        "area_ms_per_step": round(m["area_ms_per_step"], 4),
+        "full_attn_ms": round(m["full_ms"], 4),
+        "full_attn_tflops": round(m["full_tflops"], 1),
+        "full_attn_frac": round(m["full_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "speedup_vs_full": round(m["full_ms"] / m["area_ms_per_step"], 3),
+        "speedup_phase1": round(ph["speedup_phase1"], 3) if ph["speedup_phase1"] else None,
+        "speedup_phase2": round(ph["speedup_phase2"], 3) if ph["speedup_phase2"] else None,
+        "phase1_ms_per_step": round(ph["phase1_ms_per_step"], 4),
+        "phase2_ms_per_step": round(ph["phase2_ms_per_step"], 4),
+        "phase1_tflops": round(ph["phase1_tflops"], 1), "phase1_frac": round(ph["phase1_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "phase2_tflops": round(ph["phase2_tflops"], 1), "phase2_frac": round(ph["phase2_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "coarse_kernel_tflops": round(ph["coarse_kernel_tflops"], 1),
+        "coarse_kernel_frac": round(ph["coarse_kernel_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "window_kernel_tflops": round(ph["window_kernel_tflops"], 1),
+        "window_kernel_frac": round(ph["window_kernel_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "area_tflops": round(m["area_tflops"], 1), "area_frac": round(m["area_tflops"] / PEAK_MFMA_TFLOPS, 4),
+        "pool_gbs": round(ph["pool_gbs"], 1), "pool_frac_hbm": round(ph["pool_gbs"] / PEAK_HBM_GBS, 4),
+        "cpu_oracle": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +369,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="flux-6144")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configured workloads (each is timed in the same run by default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one elementwise kernel over 512 MiB before the warm-up (known "
                          "traffic, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -273,66 +395,19 @@ def main():
     A.lib()
     dev = torch.device("cuda:0")
     wl = W.get(args.workload)
-    p = A.problem_for(wl)
-    B, H, N, D = wl.B, wl.H, wl.N, wl.D
-    BH = B * H
-
-    log(f"[bench] generating {wl.name} inputs on the GPU")
-    q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
-    lat = torch.from_numpy(W.make_latent(wl)).to(dev)
-    out = torch.empty_like(q)
     ev = HipEvents()
-    sc = Schedule(A, wl, p, q, k, v, lat, out, ev)
-    torch.cuda.synchronize()
 
     if args.ablation:
+        p = A.problem_for(wl)
+        q, k, v = W.make_qkv(wl, device="cuda", dtype="bf16")
+        lat = torch.from_numpy(W.make_latent(wl)).to(dev)
+        sc = Schedule(A, wl, p, q, k, v, lat, torch.empty_like(q), ev)
         run_ablation(A, wl, sc, args)
         return
 
-    log("[bench] counting algorithmic work")
-    flops = sc.count()
-    sched, n_steps = sc.sched, sc.n_steps
-
-    if args.copy_calibration:
-        # one elementwise kernel with a unique name: reads 512 MiB, writes 512 MiB
-        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
-        log("[bench] calibration kernel (bitwise_not): 512 MiB read, 512 MiB written")
-        del src, dst
-
-    log(f"[bench] warmup x{args.warmup}")
-    for _ in range(args.warmup):
-        sc.one_pass([])
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing x{args.steps}")
-    recs = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        sc.one_pass(recs)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-
-    K = args.steps
-    agg, per_step, area_ms = sc.summarize(recs, K)
-    area_ms_per_step = area_ms / n_steps
-    n_coarse = sum(1 for st in sched if st["phase"] == A.PHASE_COARSE)
-    n_win = n_steps - n_coarse
-    coarse_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_COARSE)
-    win_fl = sum(flops[s] for s in flops if sched[s]["phase"] == A.PHASE_WINDOW)
-    win_tflops = tflops(win_fl, agg["window_kernel"])
-    coarse_tflops = tflops(coarse_fl, agg["coarse_kernel"])
-    full_ms = agg["full_call"]
-    full_tflops = tflops(sc.full_flops, agg["full_kernel"])
-    area_tflops = tflops(coarse_fl + win_fl, area_ms)
-    # pooling bytes (mean mode): read K and V (bf16), write pooled K and V (fp32)
-    pool_bytes = sum(2 * BH * N * D * 2 + 2 * BH * (N // sched[s]["f"] ** 2) * D * 4
-                     for s in range(n_steps) if sched[s]["phase"] == A.PHASE_COARSE)
-    dwt_bytes = n_win * (wl.C * N * 4 + (N // 4) * 8)
+    sc, m = measure(A, W, wl, dev, ev, args.steps, args.warmup, calibrate=args.copy_calibration)
+    agg_win_ms = m["phases"]["window_kernel_avg_ms"]
+    win_tflops = m["phases"]["window_kernel_tflops"]
 
     # ---- the matrix-core rate this GPU sustains (register-only MFMA stream) and a plain
     # read+write stream rate (torch's elementwise bitwise_not over 1 GiB in, 1 GiB out), for context
@@ -354,50 +429,54 @@ def main():
     # ---- CPU oracle baseline on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, p, q, k, v, lat, sched, flops, sc.win_pairs, n_steps)
+        p, q, k, v, lat = m["tensors"]
+        cpu = cpu_baseline(wl, q, k, v, lat, sc.sched, m["flops"], sc.win_pairs, sc.full_flops,
+                           coarse_rows=wl.N, rows=4096, full_rows=2048)
+    headline = config_summary(wl, m, None)
 
-    phases = {
-        "pool_ms_per_call": agg["pool"] / max(n_coarse, 1),
-        "coarse_ms_per_call": agg["coarse_call"] / max(n_coarse, 1),
-        "coarse_kernel_tflops": coarse_tflops,
-        "dwt_ms_per_call": agg["dwt"] / max(n_win, 1),
-        "plan_ms_per_call": agg["plan"] / max(n_win, 1),
-        "window_ms_per_call": agg["window_call"] / max(n_win, 1),
-        "window_kernel_tflops": win_tflops,
-        "pool_gbs": pool_bytes / (agg["pool"] * 1e-3) / 1e9 if agg["pool"] > 0 else 0.0,
-        "dwt_gbs": dwt_bytes / (agg["dwt"] * 1e-3) / 1e9 if agg["dwt"] > 0 else 0.0,
-        # per-phase speedups: full attention over one Phase I step (pool + coarse) and over one
-        # Phase II step (DWT map + plan + windowed attention), averaged over each phase's steps
-        "speedup_phase1": (full_ms * n_coarse / (agg["pool"] + agg["coarse_call"])
-                           if agg["pool"] + agg["coarse_call"] > 0 else None),
-        "speedup_phase2": (full_ms * n_win / (agg["dwt"] + agg["plan"] + agg["window_call"])
-                           if agg["dwt"] + agg["plan"] + agg["window_call"] > 0 else None),
-        "per_step_ms": [round(sum(per_step[s]) / len(per_step[s]), 3) for s in sorted(per_step)],
-        "per_step": sc.step_detail,
-        "schedule_tflop": (coarse_fl + win_fl) / 1e12,
-    }
+    # ---- every other configured workload, measured in the same run
+    configs = {}
+    if not args.no_configs:
+        del sc
+        m.pop("tensors")
+        torch.cuda.empty_cache()
+        for name in OTHER_CONFIGS:
+            if name == wl.name:
+                continue
+            cwl = W.get(name)
+            csc, cm = measure(A, W, cwl, dev, ev, max(1, min(args.steps, 3)), 1)
+            ccpu = None
+            if not args.no_cpu_baseline:
+                p_, q_, k_, v_, lat_ = cm["tensors"]
+                ccpu = cpu_baseline(cwl, q_, k_, v_, lat_, csc.sched, cm["flops"], csc.win_pairs, csc.full_flops,
+                                    coarse_rows=2048, rows=2048, full_rows=1024)
+            configs[name] = config_summary(cwl, cm, ccpu)
+            del csc, cm
+            torch.cuda.empty_cache()
+
+    ph = m["phases"]
     result = {
         "metric": METRIC,
-        "value": round(area_ms_per_step, 4),
+        "value": round(m["area_ms_per_step"], 4),
         "unit": "ms/step",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 3),
+        "ms_per_step": round(m["wall_ms_per_pass"], 3),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "grid": [wl.Gh, wl.Gw], "batch": B, "heads": H, "head_dim": D,
-                   "coarse_steps": n_coarse, "window_steps": n_win, "pool": "mean",
+        "config": {"workload": wl.name, "grid": [wl.Gh, wl.Gw], "batch": wl.B, "heads": wl.H, "head_dim": wl.D,
+                   "coarse_steps": m["n_coarse"], "window_steps": m["n_win"], "pool": "mean",
                    "halo": wl.halo, "bridge_k": wl.bridge_k, "io": "bf16"},
-        "area_tflops": round(area_tflops, 2),
-        "area_pct_mfma_peak": round(100.0 * area_tflops / PEAK_MFMA_TFLOPS, 2),
-        "full_attn_ms": round(full_ms, 3),
-        "full_attn_tflops": round(full_tflops, 2),
-        "speedup_vs_full": round(full_ms / area_ms_per_step, 3),
-        "phases": {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in phases.items()},
+        "area_tflops": round(m["area_tflops"], 2),
+        "area_pct_mfma_peak": round(100.0 * m["area_tflops"] / PEAK_MFMA_TFLOPS, 2),
+        "full_attn_ms": round(m["full_ms"], 3),
+        "full_attn_tflops": round(m["full_tflops"], 2),
+        "speedup_vs_full": round(m["full_ms"] / m["area_ms_per_step"], 3),
+        "phases": rounded(ph),
         "roofline": {
             "kernel": "attn_kernel (windowed)",
             "bound": "mfma",
@@ -406,18 +485,19 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(win_tflops / PEAK_MFMA_TFLOPS, 4),
             "traffic": measured_traffic(wl.name),
-            "launches_per_step": n_win,
-            "avg_launch_ms": round(agg["window_kernel"] / max(n_win, 1), 4),
+            "launches_per_step": m["n_win"],
+            "avg_launch_ms": round(agg_win_ms, 4),
         },
         "cpu_baseline": cpu,
         "measured_peak": {
             "what": "register-only v_mfma_f32_32x32x16_f16 stream on this GPU (area_measure_mfma_peak)",
             "mfma_tflops": round(mfma_measured, 1),
             "window_kernel_frac": round(win_tflops / mfma_measured, 4) if mfma_measured > 0 else None,
-            "full_attn_frac": round(full_tflops / mfma_measured, 4) if mfma_measured > 0 else None,
+            "full_attn_frac": round(m["full_tflops"] / mfma_measured, 4) if mfma_measured > 0 else None,
             "copy_gbs": round(copy_gbs, 1) if copy_gbs > 0 else None,
-            "pool_frac_of_copy": round(phases["pool_gbs"] / copy_gbs, 4) if copy_gbs > 0 else None,
+            "pool_frac_of_copy": round(ph["pool_gbs"] / copy_gbs, 4) if copy_gbs > 0 else None,
         },
+        "configs": dict({wl.name: dict(headline, note="the headline workload above")}, **configs),
     }
     print(json.dumps(result), flush=True)
 
@@ -488,11 +568,17 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
-    """The oracle on head 0 of three steps (the first coarse step, the middle
-    and the last window step), scaled by algorithmic work to the whole
-    schedule and all heads: each phase's steps take the sampled steps'
-    seconds per FLOP of that phase."""
+def cpu_baseline(wl, q, k, v, lat, sched, flops, win_pairs, full_flops, coarse_rows, rows, full_rows):
+    """The float64 NumPy oracle on head 0 of the workload, timed on the host:
+    the Phase I step at the first pooling factor, Phase II steps 0, 1 and
+    S-1 (Haar map, plan, bridge and windowed attention) and full attention,
+    each on a bounded sample of query rows (coarse_rows, rows, full_rows;
+    all rows when the grid is smaller).  Each attention call is timed twice,
+    with one row and with the sample: the one-row time is the call's fixed
+    part (the key rotation of the head), counted once per head; the rest is
+    scaled by algorithmic FLOPs to all rows and heads.  Map and plan time is
+    counted once per step, pooling and bridge once per head.  Unsampled steps
+    take the seconds per FLOP of their phase's nearest sample."""
     import numpy as np
     import resolution_diffusion_transformer_amd as A
     from oracle import area_oracle as O
@@ -501,42 +587,101 @@ def cpu_baseline(wl, p, q, k, v, lat, sched, flops, win_pairs, n_steps):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    log("[bench] cpu baseline: oracle on head 0 of the first coarse, the middle and the last window step")
+    H = wl.B * wl.H
+    N, D = wl.N, wl.D
+    log(f"[bench] cpu baseline ({wl.name}): oracle on head 0, sampled query rows")
     qh = q[:, :1].float().cpu().numpy().astype(np.float64)
     kh = k[:, :1].float().cpu().numpy().astype(np.float64)
     vh = v[:, :1].float().cpu().numpy().astype(np.float64)
     latn = lat.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(7))
+    O.attention(qh[0, 0, :1024], kh[0, 0, :1024], vh[0, 0, :1024])  # BLAS thread warm-up, untimed
+
+    def pick(n):
+        return np.arange(N) if n >= N else np.sort(rng.choice(N, size=n, replace=False))
+
+    def two_times(fn, r):
+        """(fixed seconds, seconds of the sample beyond the fixed part)"""
+        t0 = time.perf_counter()
+        fn(r[:1])
+        t1 = time.perf_counter()
+        fn(r)
+        t2 = time.perf_counter()
+        return t1 - t0, max((t2 - t1) - (t1 - t0), 1e-9), t2 - t0
+
     coarse = [s for s, st in enumerate(sched) if st["phase"] == A.PHASE_COARSE]
     window = [s for s, st in enumerate(sched) if st["phase"] == A.PHASE_WINDOW]
-    c_samples = coarse[:1]
-    w_samples = sorted({window[len(window) // 2], window[-1]}) if window else []
-    t_c = 0.0
-    for s_c in c_samples:
-        f = sched[s_c]["f"]
+    detail, measured = [], 0.0
+    est_ms = {}
+    # Phase I at the first pooling factor: pooling of the whole head, attention of the sampled rows
+    if coarse:
+        s = coarse[0]
+        f = sched[s]["f"]
+        r = pick(coarse_rows)
         t0 = time.perf_counter()
         kp, vp = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, O.POOL_MEAN, wl.rope_theta)
-        O.coarse_attention(qh, kp, vp, wl.Gh, wl.Gw, f, wl.rope_theta)
-        t_c += time.perf_counter() - t0
-    t_w = 0.0
-    Eq = O.energy_fixed(O.detail_energy(latn)) if w_samples else None
-    for s_w in w_samples:
+        t_pool = time.perf_counter() - t0
+        t_fix, t_var, t_all = two_times(lambda rr: O.coarse_attention(qh, kp, vp, wl.Gh, wl.Gw, f, wl.rope_theta,
+                                                                      rows=rr), r)
+        measured += t_pool + t_all
+        per_flop = t_var / (4.0 * D * max(len(r) - 1, 1) * (N // (f * f)))
+        for c in coarse:
+            est_ms[c] = 1e3 * (H * (t_pool + t_fix) + per_flop * flops[c])
+        detail.append({"step": s, "phase": "coarse", "f": f, "rows": int(len(r)), "measured_s": round(t_pool + t_all, 3),
+                       "est_ms_all_heads": round(est_ms[s], 1)})
+    # Phase II steps 0, 1 and S-1
+    win_rate = []
+    for s in sorted({window[0], window[min(1, len(window) - 1)], window[-1]}) if window else []:
+        t = s - wl.p1_steps
+        w = sched[s]["w"]
+        R = sched[s]["R"]
+        r = pick(rows)
         t0 = time.perf_counter()
-        t = s_w - wl.p1_steps
-        plan = O.window_plan(wl.Gh, wl.Gw, sched[s_w]["w"], wl.halo, wl.seed, t, Eq)
-        br = O.bridge_select(kh[0, 0], wl.bridge_k, wl.Gh, wl.Gw)[None, None]
-        O.window_attention(qh, kh, vh, plan, br, wl.Gh, wl.Gw, wl.rope_theta)
-        t_w += time.perf_counter() - t0
-    H = wl.H * wl.B
-    # the samples are one head; their seconds per FLOP move them along each phase, H scales to all heads
-    coarse_total = (H * t_c * sum(flops[s] for s in coarse) / sum(flops[s] for s in c_samples)) if c_samples else 0.0
-    win_total = (H * t_w * sum(flops[s] for s in window) / sum(flops[s] for s in w_samples)) if w_samples else 0.0
-    ms_per_step = (coarse_total + win_total) * 1e3 / n_steps
+        Eq = O.energy_fixed(O.detail_energy(latn))
+        plan = O.window_plan(wl.Gh, wl.Gw, w, wl.halo, wl.seed, t, Eq)
+        t1 = time.perf_counter()
+        br = O.bridge_select(kh[0, 0], R, wl.Gh, wl.Gw) if R > 0 else None
+        t2 = time.perf_counter()
+        brr = None if br is None else br[None, None]
+        t_fix, t_var, t_all = two_times(lambda rr: O.window_attention(qh, kh, vh, plan, brr, wl.Gh, wl.Gw,
+                                                                      wl.rope_theta, rows=rr), r)
+        measured += (t2 - t0) + t_all
+        sel = np.zeros(N, dtype=bool)
+        sel[r[1:]] = True  # the rows beyond the one-row call
+        sel[r[0]] = False
+        pairs = 0
+        for win in plan.windows:
+            nsel = int(sel[O.window_query_indices(win, wl.Gw)].sum())
+            if nsel:
+                pairs += nsel * len(O.window_key_indices(win, wl.Gw, br))
+        per_flop = t_var / (4.0 * D * max(pairs, 1))
+        win_rate.append((s, per_flop, t1 - t0, (t2 - t1) + t_fix))
+        est_ms[s] = 1e3 * ((t1 - t0) + H * ((t2 - t1) + t_fix) + per_flop * flops[s])
+        detail.append({"step": s, "phase": "window", "w": w, "rows": int(len(r)),
+                       "measured_s": round((t2 - t0) + t_all, 3), "est_ms_all_heads": round(est_ms[s], 1)})
+    for s in window:
+        if s in est_ms:
+            continue
+        _, per_flop, t_plan, t_head = min(win_rate, key=lambda e: abs(e[0] - s))
+        est_ms[s] = 1e3 * (t_plan + H * t_head + per_flop * flops[s])
+    # full attention: sampled rows of head 0, scaled to every row and head
+    r = pick(full_rows)
+    t_fix, t_var, t_all = two_times(lambda rr: O.full_attention(qh, kh, vh, wl.Gh, wl.Gw, wl.rope_theta, rows=rr), r)
+    measured += t_all
+    full_ms = 1e3 * (H * t_fix + t_var * full_flops / (4.0 * D * max(len(r) - 1, 1) * N))
+    ms_per_step = sum(est_ms.values()) / max(len(est_ms), 1)
     return {"value": round(ms_per_step, 1), "unit": "ms/step", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle on head 0 of {H}: coarse step {c_samples} (all {wl.N} queries) took "
-                       f"{t_c:.2f} s; window steps {w_samples} (w={[sched[s]['w'] for s in w_samples]}, plan + "
-                       f"bridge + attention, all queries) took {t_w:.2f} s; each phase scaled by its samples' "
-                       f"seconds per algorithmic FLOP to all {n_steps} steps and {H} heads"),
-            "sample_seconds": round(t_c + t_w, 2)}
+            "sample": (f"float64 NumPy oracle on head 0 of {H}: Phase I step at f0 ({min(coarse_rows, N)} query "
+                       f"rows), Phase II steps 0, 1 and S-1 ({min(rows, N)} sampled query rows each, with the step's "
+                       f"Haar map, plan and bridge), full attention ({min(full_rows, N)} rows); a one-row call gives "
+                       f"each call's fixed part (counted per head), the rest is scaled by FLOPs to all {N} rows and "
+                       f"{H} heads; unsampled steps take their phase's seconds per FLOP; {len(est_ms)} steps"),
+            "sample_seconds": round(measured, 2),
+            "steps": detail,
+            "full_attn_ms_est": round(full_ms, 1),
+            "full_attn_note": (f"head 0, {min(full_rows, N)} of {N} query rows timed, scaled to all rows and x{H} "
+                               f"heads (extrapolated)"),
+            "speedup_vs_full_oracle": round(full_ms / ms_per_step, 3) if ms_per_step > 0 else None}
 
 
 if __name__ == "__main__":

@@ -1313,8 +1313,9 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
   if (g > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "attention grid too large");
   b.grid = (int)g;
   dim3 grid((unsigned)b.grid);
-  // the scaled kernel's work-groups walk the listed items (one per CU fits)
-  dim3 grid_scaled((unsigned)std::min<int64_t>(g, 1024));
+  // the scaled kernel's work-groups walk the listed items, one work-group
+  // per CU (the register budget of one fits a CU)
+  dim3 grid_scaled((unsigned)std::min<int64_t>(g, 256));
   AttnEvents ev = attn_events();
   if (ev.begin) {
     hipError_t e = hipEventRecord((hipEvent_t)ev.begin, st);

@@ -220,7 +220,7 @@ struct BridgeWs {
 int n_chunks(int N) { return (N + kBridgeChunk - 1) / kBridgeChunk; }
 
 // Keys saturate at this magnitude inside the mean-key sum only.
-constexpr double kMeanClamp = 268435456.0;  // 2^28
+constexpr float kMeanClamp = 268435456.0f;  // 2^28, exact in fp32
 
 BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
   BridgeWs b;
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict
     const unsigned u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      double lo = fmin(fmax((double)__uint_as_float(u[i] << 16), -kMeanClamp), kMeanClamp);
-      double hi = fmin(fmax((double)__uint_as_float(u[i] & 0xFFFF0000u), -kMeanClamp), kMeanClamp);
+      double lo = (double)fminf(fmaxf(__uint_as_float(u[i] << 16), -kMeanClamp), kMeanClamp);
+      double hi = (double)fminf(fmaxf(__uint_as_float(u[i] & 0xFFFF0000u), -kMeanClamp), kMeanClamp);
       acc[2 * i] += (long long)rint(lo * 16777216.0);
       acc[2 * i + 1] += (long long)rint(hi * 16777216.0);
     }
