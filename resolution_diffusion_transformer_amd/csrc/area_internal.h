@@ -115,6 +115,7 @@ int launch_bridge(const void* k, int32_t* idx, int64_t BH, int T, int Gh, int Gw
                   int rw, void* ws, stream_t s);
 constexpr int kBridgeSortMax = 4096;  // cells per row of the bridge cell grid
 size_t bridge_ws_bytes(int64_t BH, int N, int D, int R);
+int bridge_chunks(int N);             // kBridgeChunk-row partial sums of the mean key
 
 // Dense key/value operands, one 64-key tile per work-group: fp16 key rows
 // kr[bh][M][D] and fp16 V^T tiles vt[bh][t][d][k] = v[bh][64 t + k][d]

@@ -1339,10 +1339,6 @@ int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
 
 }  // namespace
 
-size_t vt_bytes(int64_t BH, int M, int D) { return (size_t)BH * ((M + BN - 1) / BN) * BN * D * 2; }
-
-size_t tile_exp_bytes(int64_t BH, int M) { return (size_t)BH * ((M + BN - 1) / BN) * sizeof(int); }
-
 int launch_kv_tiles(const void* k, const void* v, const void* rope, void* kr, void* vt, int* kexp, int* vexp,
                     int* flags, int64_t BH, int M, int D, bool f32_in, int T, int Gw, stream_t s) {
   if (BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
@@ -1396,12 +1392,6 @@ int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int G
   a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
   if (Nq == 0) return AREA_OK;
   return launch_attn<false>(a, D, (int64_t)a.n_qtiles * BH, (hipStream_t)s);
-}
-
-size_t window_items_ws_bytes(int max_windows, int64_t max_items, int n_base, int64_t max_gtiles) {
-  return align_up(2 * sizeof(int)) + 2 * align_up(sizeof(int) * (max_windows > 0 ? max_windows : 1)) +
-         align_up(sizeof(int) * (n_base > 0 ? n_base : 1)) + align_up(sizeof(int) * 2 * (max_items > 0 ? max_items : 1)) +
-         align_up(sizeof(int) * 2 * (max_gtiles > 0 ? max_gtiles : 1));
 }
 
 int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32_t* wsum, const int32_t* bridge_idx,

@@ -329,8 +329,6 @@ static dim3 grid_2d(int64_t per_bh, int64_t BH) {
   return dim3((unsigned)gx, (unsigned)gy);
 }
 
-size_t rope_table_bytes(int Gh, int Gw, int D) { return 2 * (size_t)std::max(Gh, Gw) * (D / 4) * sizeof(float2); }
-
 int launch_rope_table(void* tab, int Gh, int Gw, int D, float theta, float div, int* flags, int64_t n_flags,
                       stream_t s) {
   const int P = std::max(Gh, Gw), NF = D / 4;

@@ -217,8 +217,6 @@ struct BridgeWs {
   int* cell;
 };
 
-int n_chunks(int N) { return (N + kBridgeChunk - 1) / kBridgeChunk; }
-
 // Keys saturate at this magnitude inside the mean-key sum only.
 constexpr float kMeanClamp = 268435456.0f;  // 2^28, exact in fp32
 
@@ -226,7 +224,7 @@ BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
   BridgeWs b;
   char* p = (char*)ws;
   b.part = (long long*)p;
-  p += align_up(sizeof(long long) * BH * n_chunks(N) * D);
+  p += align_up(sizeof(long long) * BH * bridge_chunks(N) * D);
   b.mean = (double*)p;
   p += align_up(sizeof(double) * BH * D);
   b.cell = (int*)p;
@@ -393,10 +391,6 @@ __global__ __launch_bounds__(1024) void bridge_sort_kernel(const int* __restrict
 
 }  // namespace
 
-size_t plan_ws_bytes(int n_base) {
-  return align_up(sizeof(long long) * (n_base + 1)) + align_up(sizeof(int) * (n_base > 0 ? n_base : 1));
-}
-
 int launch_plan(const PlanArgs& a, const int32_t* energy_q, int32_t* plan, int32_t* wsum, void* ws,
                 stream_t s) {
   hipStream_t st = (hipStream_t)s;
@@ -416,18 +410,12 @@ int launch_plan(const PlanArgs& a, const int32_t* energy_q, int32_t* plan, int32
   return check_launch("plan_wsum_kernel");
 }
 
-size_t bridge_ws_bytes(int64_t BH, int N, int D, int R) {
-  if (R <= 0) return 0;
-  return align_up(sizeof(long long) * BH * n_chunks(N) * D) + align_up(sizeof(double) * BH * D) +
-         align_up(sizeof(int) * BH * R);
-}
-
 int launch_bridge(const void* k, int32_t* idx, int64_t BH, int T, int Gh, int Gw, int D, int R, int rh, int rw,
                   void* ws, stream_t s) {
   hipStream_t st = (hipStream_t)s;
   int N = Gh * Gw;
   BridgeWs b = bridge_ws(ws, BH, N, D, R);
-  int nch = n_chunks(N);
+  int nch = bridge_chunks(N);
   if (BH > 65535) return fail(AREA_E_UNSUPPORTED, "batch*heads above 65535");
   if (D == 128)
     hipLaunchKernelGGL(bridge_sum_kernel<128>, dim3(nch, (unsigned)BH), dim3(256), 0, st, (const uint4*)k, b.part, N,
