@@ -311,6 +311,19 @@ int area_window_plan(const area_problem* p, int step, const int32_t* energy_q, c
                      int32_t* plan, int32_t* wsum, int32_t* bridge_idx,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* area_window_plan for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation): the same
+ * kernels and outputs, with the plan's scratch in the library's own static
+ * device array (16 MiB per GPU, held until the process ends) instead of a
+ * workspace argument.  Returns AREA_E_WORKSPACE when
+ * area_workspace_bytes(p, AREA_OP_PLAN) exceeds 16 MiB (about B*H*Gh*Gw*D/128
+ * bytes with a bridge), AREA_E_HIP if the array cannot be resolved on the
+ * current device, else as area_window_plan.  Allocates nothing.  Every call
+ * on one GPU uses that GPU's array: calls that may overlap on one GPU
+ * (unordered streams) race and must be serialised by the caller. */
+int area_window_plan_static(const area_problem* p, int step, const int32_t* energy_q, const void* k,
+                            int32_t* plan, int32_t* wsum, int32_t* bridge_idx, void* stream);
+
 /* Phase II windowed attention with blending (ai.info summary, Methodology,
  * Phase II).  For every window of `plan`: its queries attend to the keys of
  * its Halo rectangle plus the bridge tokens outside that rectangle, RoPE at

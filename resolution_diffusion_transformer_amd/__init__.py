@@ -18,7 +18,7 @@ __all__ = [
     "AreaError", "Problem", "lib", "library_path", "exported_symbols",
     "area_validate", "area_step_info", "area_f0", "area_base_windows", "area_workspace_bytes",
     "area_plan_words", "area_pool_kv", "area_coarse_attn", "area_dwt_detail",
-    "area_window_plan", "area_window_attn", "area_full_attn", "area_text_attn", "area_attn_step",
+    "area_window_plan", "area_window_plan_static", "area_window_attn", "area_full_attn", "area_text_attn", "area_attn_step",
     "area_set_attn_events",
     "POOL_MEAN", "POOL_CENTER", "POOL_MEDOID", "POOL_RANDOM", "PHASE_FULL", "PHASE_COARSE", "PHASE_WINDOW",
     "OP_FULL", "OP_COARSE", "OP_PLAN", "OP_WINDOW", "OP_STEP", "PLAN_HEADER", "PLAN_REC",
@@ -130,6 +130,7 @@ _SIGS = {
     "area_dwt_detail": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 4),
     "area_window_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 6
                          + [ctypes.c_size_t, ctypes.c_void_p]),
+    "area_window_plan_static": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 6),
     "area_window_attn": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 8
                          + [ctypes.c_size_t, ctypes.c_void_p]),
     "area_full_attn": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_void_p] * 5
@@ -349,6 +350,32 @@ def area_window_plan(p: Problem, step: int, energy_q, k, plan=None, wsum=None, b
     _check(lib().area_window_plan(ref, step, _ptr(energy_q), _ptr(k), _ptr(plan), _ptr(wsum),
                                   _ptr(bridge_idx) if use_bridge else None, _ptr(ws),
                                   _nbytes(ws), _stream()))
+    return plan, wsum, (bridge_idx if use_bridge else None)
+
+
+def area_window_plan_static(p: Problem, step: int, energy_q, k, plan=None, wsum=None, bridge_idx=None):
+    """area_window_plan with the library's static device scratch (no workspace)."""
+    torch = _torch()
+    src = energy_q if energy_q is not None else k
+    dev = src.device if src is not None else torch.device("cuda")
+    if energy_q is not None:
+        _need(energy_q, torch.int32, (p.Gh // 2, p.Gw // 2), "energy_q")
+    if k is not None:
+        _need(k, torch.bfloat16, (p.B, p.H, p.L, p.D), "k")
+    words = area_plan_words(p)
+    plan = torch.zeros(words, dtype=torch.int32, device=dev) if plan is None else plan
+    wsum = torch.empty(p.N, dtype=torch.int32, device=dev) if wsum is None else wsum
+    R = area_step_info(p, step)["R"]
+    use_bridge = k is not None and R > 0
+    if use_bridge and bridge_idx is None:
+        bridge_idx = torch.empty((p.B, p.H, R), dtype=torch.int32, device=dev)
+    _need(plan, torch.int32, (words,), "plan")
+    _need(wsum, torch.int32, (p.N,), "wsum")
+    if use_bridge:
+        _need(bridge_idx, torch.int32, (p.B, p.H, R), "bridge_idx")
+    s, ref = _pp(p)
+    _check(lib().area_window_plan_static(ref, step, _ptr(energy_q), _ptr(k), _ptr(plan), _ptr(wsum),
+                                         _ptr(bridge_idx) if use_bridge else None, _stream()))
     return plan, wsum, (bridge_idx if use_bridge else None)
 
 

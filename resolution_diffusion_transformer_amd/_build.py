@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libarea.so")
 
-SOURCES = ["area_host.cpp", "area_sizes.cpp", "k_elementwise.hip", "k_plan.hip", "k_attn.hip", "k_probe.hip"]
+SOURCES = ["area_host.cpp", "area_sizes.cpp", "k_elementwise.hip", "k_plan.hip", "k_attn.hip", "k_probe.hip", "area_static.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,

@@ -175,3 +175,17 @@ int measure_mfma_peak(void* sink, double* tflops, void*) {
 }
 
 }  // namespace area
+
+// Host stand-in of the static-scratch plan call (the library's device array
+// lives in a HIP source this build leaves out): the same validation and
+// size limit, with a host array in place of the device one.
+extern "C" int area_window_plan_static(const area_problem* p, int step, const int32_t* energy_q, const void* k,
+                                       int32_t* plan, int32_t* wsum, int32_t* bridge_idx, void* stream) {
+  constexpr size_t kScratchBytes = (size_t)16 << 20;
+  alignas(256) static unsigned char scratch[kScratchBytes];
+  int rc = area_validate(p);
+  if (rc) return rc;
+  if (area_workspace_bytes(p, AREA_OP_PLAN) > kScratchBytes)
+    return area::fail(AREA_E_WORKSPACE, "the plan needs more than the static scratch");
+  return area_window_plan(p, step, energy_q, k, plan, wsum, bridge_idx, scratch, kScratchBytes, stream);
+}
