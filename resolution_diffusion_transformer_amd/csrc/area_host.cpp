@@ -475,7 +475,7 @@ static int dense_pass(const area_problem& p, char* b, const void* q, const void*
   int* kexp = (int*)(b + l.kexp);
   int* vexp = (int*)(b + l.vexp);
   int* flags = (int*)(b + l.flags);
-  int rc = launch_rope_table(b + l.tab, p.Gh, p.Gw, p.D, p.rope_theta, 1.0f, flags, BH + 1, stream);
+  int rc = launch_rope_table(b + l.tab, p.Gh, p.Gw, p.D, p.rope_theta, 1.0f, flags, range_clear_words(BH), stream);
   if (rc) return rc;
   rc = launch_kv_tiles(k, v, b + l.tab, b + l.kr, b + l.vt, kexp, vexp, flags, BH, L, p.D, false, p.T, p.Gw, stream);
   if (rc) return rc;
@@ -626,7 +626,7 @@ int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp
   int* vexp = (int*)(b + l.vexp);
   int* flags = (int*)(b + l.flags);
   // queries turn at coarse-grid positions (row / f, column / f), as the keys
-  rc = launch_rope_table(b + l.tab, p->Gh, p->Gw, p->D, p->rope_theta, (float)f, flags, BH + 1, stream);
+  rc = launch_rope_table(b + l.tab, p->Gh, p->Gw, p->D, p->rope_theta, (float)f, flags, range_clear_words(BH), stream);
   if (rc) return rc;
   rc = launch_kv_tiles(kp, vp, b + l.tab, b + l.kr, b + l.vt, kexp, vexp, flags, BH, M, p->D, true, p->T, p->Gw,
                        stream);
@@ -761,7 +761,7 @@ int area_window_attn(const area_problem* p, int step, const int32_t* plan, const
   w.kexp = (int*)(base + l.kexp);
   w.vexp = (int*)(base + l.vexp);
   w.flags = (int*)(base + l.flags);
-  rc = launch_rope_table(base + l.rope, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, w.flags, BH_of(*p) + 1, stream);
+  rc = launch_rope_table(base + l.rope, p->Gh, p->Gw, p->D, p->rope_theta, 1.0f, w.flags, range_clear_words(BH_of(*p)), stream);
   if (rc) return rc;
   return launch_window_attn(a, plan, wsum, a.R ? bridge_idx : nullptr, q, k, v, base + l.rope, out, w, stream);
 }

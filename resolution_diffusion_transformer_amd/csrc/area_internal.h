@@ -139,10 +139,12 @@ int launch_kv_tiles(const void* k, const void* v, const void* rope, void* kr, vo
 int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int Gw, const void* k_rot,
                       const void* vt, const int* kexp, const int* vexp, int* flags, void* out, int64_t BH,
                       int Nq, int q0, int q_rows, int Nk, int D, stream_t s);
-// Words of the range region of an attention call: BH flags, then the count
-// and list of work items the scaled attention kernel runs (cleared, flags and
-// count, by the call's rope-table launch).
-inline size_t range_words(int64_t BH, int64_t work) { return (size_t)BH + 1 + (size_t)work; }
+// Words of the range region of an attention call: BH flags, the 8 per-XCD
+// work counters of the persistent attention kernel, then the count and list
+// of work items the scaled attention kernel runs.  The call's rope-table
+// launch clears the first range_clear_words (flags, counters and count).
+inline size_t range_words(int64_t BH, int64_t work) { return (size_t)BH + 8 + 1 + (size_t)work; }
+inline int64_t range_clear_words(int64_t BH) { return BH + 8 + 1; }
 
 struct WindowAttnArgs {
   int Gh, Gw, D, R;

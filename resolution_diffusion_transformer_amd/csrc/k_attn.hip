@@ -510,9 +510,9 @@ struct AttnArgs {
   const int* vexp;     // [BH][k_tiles] the same for the V^T tiles
   const int* flags;    // [BH] nonzero: some tile of the (batch, head) has a nonzero exponent
   int* redo;           // [0]: count, then the logical ids of the items the scaled kernel runs
+  int* ctr;            // [8] per-XCD work counters of the persistent plain kernel
   int n_kv;            // dense mode: keys per query
   int n_qtiles;        // dense mode: query tiles per head
-  int grid;            // launched work-groups (multiple of 8)
   float c;             // log2(e) / sqrt(D)
   // window mode
   const int32_t* plan;
@@ -795,104 +795,175 @@ __device__ __attribute__((always_inline)) inline void phase_b(f32x16 (&o)[QG][D 
 // else one.
 constexpr int kAttnGroupsPerCu = kAttnQG == 1 && kAttnWaves == 4 ? 2 : 1;
 
-// One work item (256 queries of one (batch, head): a query tile of the
-// dense sequence, or of one window record) over its whole key set.  SCALED
-// selects the loop that undoes nonzero operand exponents; the plain loop
-// hands such an item to the scaled kernel through the list a.redo.
-template <int D, bool WIN, bool SCALED>
-__device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& a, const int64_t L, u16* ks0,
-                                                                u16* vt0, u16* ks1, u16* vt1) {
-  constexpr int QG = kAttnQG;     // 32-query groups per wave
-  constexpr int BM = kAttnBM;     // kAttnWaves waves x QG groups x 32 queries
-  constexpr int KD = D / 16;
-  constexpr int DB = D / 32;
-  static_assert(BM == kAttnWaves * 32 * QG, "query tile");
+// A work item: 256 queries of one (batch, head) -- a query tile of the dense
+// sequence, or of one window record -- over the item's whole key set.  The
+// fields are wave-uniform.
+struct Item {
+  bool valid;
+  int L, bh, qtile, rec, qy0, qx0, qh, qw, nq, nkv;
+  int64_t t0;                // first key tile of the item's key set
+  const u16* kbase;
+  const u16* vtbase;
+  const u16* qbase;
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, hi = lane >> 5;
-
+template <int D, bool WIN>
+__device__ __attribute__((always_inline)) inline Item decode_item(const AttnArgs& a, int L) {
+  Item it;
+  it.valid = false;
+  it.L = L;
+  it.bh = it.qtile = it.rec = it.qy0 = it.qx0 = it.qh = it.nq = it.nkv = 0;
+  it.qw = 1;
+  it.t0 = 0;
+  it.kbase = it.vtbase = it.qbase = nullptr;
+  if (L < 0) return it;
   int64_t bh;
-  int qtile = 0, rec = 0;
-  int qy0 = 0, qx0 = 0, qh = 0, qw = 1;
-  int nq, nkv;
-  int64_t t0 = 0;  // first key tile of the item's key set
   if constexpr (WIN) {
-    bh = L / a.max_items;
-    int64_t it = L - bh * a.max_items;
-    if (bh >= a.BH || it >= a.n_items[0]) return;
-    rec = a.items[2 * it];
-    qtile = a.items[2 * it + 1];
-    const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rec;
-    qy0 = rp[0]; qx0 = rp[1]; qh = rp[2]; qw = rp[3];
-    nq = qh * qw;
-    nkv = rp[6] * rp[7] + (a.R > 0 ? a.bcount[(int64_t)rec * a.BH + bh] : 0) + a.T;
-    t0 = a.kv_tile_off[rec];
+    const int ni = a.n_items[0];  // items per (batch, head)
+    if (ni <= 0) return it;
+    bh = L / ni;
+    const int64_t k = L - bh * ni;
+    if (bh >= a.BH) return it;
+    it.rec = a.items[2 * k];
+    it.qtile = a.items[2 * k + 1];
+    const int32_t* rp = a.plan + AREA_PLAN_HEADER + AREA_PLAN_REC * it.rec;
+    it.qy0 = rp[0];
+    it.qx0 = rp[1];
+    it.qh = rp[2];
+    it.qw = rp[3];
+    it.nq = it.qh * it.qw;
+    it.nkv = rp[6] * rp[7] + (a.R > 0 ? a.bcount[(int64_t)it.rec * a.BH + bh] : 0) + a.T;
+    it.t0 = a.kv_tile_off[it.rec];
   } else {
     bh = L / a.n_qtiles;
-    qtile = (int)(L - bh * a.n_qtiles);
-    if (bh >= a.BH) return;
-    nq = a.Nq;
-    nkv = a.n_kv;
+    it.qtile = (int)(L - bh * a.n_qtiles);
+    if (bh >= a.BH) return it;
+    it.nq = a.Nq;
+    it.nkv = a.n_kv;
   }
-  const u16* kbase = a.k + bh * a.k_rows * D + t0 * BN * D;
-  const u16* vtbase = a.vt + (bh * a.k_tiles + t0) * (int64_t)D * BN;
-  const u16* qbase = a.q + (bh * (int64_t)a.q_rows + a.q0) * D;
+  it.bh = (int)bh;
+  // the buffer resources of the tile DMAs need wave-uniform bases and sizes
+  it.nkv = __builtin_amdgcn_readfirstlane(it.nkv);
+  it.kbase = uniform_ptr(a.k + bh * a.k_rows * D + it.t0 * BN * D);
+  it.vtbase = uniform_ptr(a.vt + (bh * a.k_tiles + it.t0) * (int64_t)D * BN);
+  it.qbase = a.q + (bh * (int64_t)a.q_rows + a.q0) * D;
+  it.valid = true;
+  return it;
+}
 
-  // ---- queries of this lane
-  int qtok[QG];
-  bool qvalid[QG];
+// The lane's queries of an item: token rows, validity, and the raw bf16
+// chunks with their (cos, sin), loaded ahead of the rotation so that the load
+// latency overlaps the first tile DMAs (or the previous item's epilogue).
+template <int D>
+struct Queries {
+  int qtok[kAttnQG];
+  bool qvalid[kAttnQG];
+  u32x4 qraw[kAttnQG][D / 16];
+  float4 qcs[kAttnQG][D / 16][2];
+};
+
+template <int D, bool WIN>
+__device__ __attribute__((always_inline)) inline void load_queries(const AttnArgs& a, const Item& it,
+                                                                   Queries<D>& q) {
+  constexpr int QG = kAttnQG, BM = kAttnBM, KD = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    int t = qtile * BM + wave * 32 * QG + 32 * g + n;
-    qvalid[g] = t < nq;
+    const int t = it.qtile * BM + wave * 32 * QG + 32 * g + n;
+    q.qvalid[g] = t < it.nq;
     if constexpr (WIN) {
-      int yy = qvalid[g] ? t / qw : 0;
-      int xx = qvalid[g] ? t - yy * qw : 0;
-      qtok[g] = (qy0 + yy) * a.Gw + qx0 + xx;
+      const int yy = q.qvalid[g] ? t / it.qw : 0;
+      const int xx = q.qvalid[g] ? t - yy * it.qw : 0;
+      q.qtok[g] = (it.qy0 + yy) * a.Gw + it.qx0 + xx;
     } else {
-      qtok[g] = qvalid[g] ? t : 0;
+      q.qtok[g] = q.qvalid[g] ? t : 0;
     }
   }
   // MFMA B operand: chunk 2 kd + hi (channels 16 kd + 8 hi ..) of the
   // lane's query, turned by RoPE at its grid position (chunks of the first
   // half follow the row, the others the column; text rows sit at (0, 0)).
-  // The raw chunks and their (cos, sin) are loaded here and turned after
-  // the first tile DMAs have been started, so the two latencies overlap.
-  u32x4 qraw[QG][KD];
-  float4 qcs[QG][KD][2];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    const int64_t row = (int64_t)a.q0 + qtok[g];
+    const int64_t row = (int64_t)a.q0 + q.qtok[g];
     int py = 0, px = 0;
     if (row >= a.q_text) {
       const int img = (int)(row - a.q_text);
       py = img / a.Gw;
       px = img - py * a.Gw;
     }
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(qbase + (int64_t)qtok[g] * D);
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(it.qbase + (int64_t)q.qtok[g] * D);
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd) {
       const int ch = 2 * kd + hi;
       const int pos = kd < KD / 2 ? py : px;
       // frequencies 4 (ch % KD) .. + 3: pairs 2 (ch % KD) and 2 (ch % KD) + 1
       const float4* cs = a.rope + (int64_t)(2 * (ch % KD)) * a.rope_P + pos;
-      qraw[g][kd] = qrow[ch];
-      qcs[g][kd][0] = cs[0];
-      qcs[g][kd][1] = cs[a.rope_P];
+      q.qraw[g][kd] = qrow[ch];
+      q.qcs[g][kd][0] = cs[0];
+      q.qcs[g][kd][1] = cs[a.rope_P];
     }
   }
-  f16x8 qf[QG][KD];
-  int eq[QG];         // per query row: operands carry q * log2(e)/sqrt(D) * 2^-eq
-  int ev_cur = 0;     // V^T unit: O holds O_true * 2^-ev_cur (scaled loop)
-  float lsc = 1.0f;   // 2^-d of the tile whose P is turned next (scaled loop)
+}
 
+// DMAs of an item's first tiles: K tile 0 and V^T tile 0 into stage 0, K
+// tile 1 (or 0 again) into stage 1.
+template <int D>
+__device__ __attribute__((always_inline)) inline void issue_first(const Item& it, u16* ks0, u16* vt0, u16* ks1) {
+  const int tid = threadIdx.x;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = (it.nkv + BN - 1) / BN;
+  issue_k<D>(ks0, 0, tid, wave_u, it.nkv, it.kbase);
+  issue_v<D>(vt0, 0, tid, wave_u, it.vtbase);
+  issue_k<D>(ks1, min(1, nt - 1), tid, wave_u, it.nkv, it.kbase);
+}
+
+// Claims the next work item from the per-XCD counters ctr[8]: logical ids
+// x * per .. x * per + per - 1 (those below total) belong to XCD x; an XCD
+// whose share is spent takes from the others in turn.  raw is the value this
+// work-group already drew from its own XCD's counter.  -1 when every share is
+// spent.
+__device__ inline int claim_from(int* ctr, int xcd, int per, int64_t total, int raw) {
+  if (raw < per && (int64_t)xcd * per + raw < total) return xcd * per + raw;
+  for (int k = 1; k < 8; ++k) {
+    const int x = (xcd + k) & 7;
+    const int i = atomicAdd(&ctr[x], 1);
+    if (i < per && (int64_t)x * per + i < total) return x * per + i;
+  }
+  return -1;
+}
+
+// Everything of an item between its query loads and its epilogue: rotation
+// of the queries (with their exponents), then, unless the item needs the
+// scaled loop (the plain kernel lists it and returns true), the first tile's
+// scores and the software-pipelined loop over the key tiles.  The plain
+// kernel also resolves the next item here: `fut` (thread 0's draw from its
+// XCD's counter) becomes `look`, shared through s_next.
+template <int D, bool WIN, bool SCALED>
+__device__ __attribute__((always_inline)) inline bool compute_item(
+    const AttnArgs& a, const Item& it, Queries<D>& qs, u16* ks0, u16* vt0, u16* ks1, u16* vt1,
+    f32x16 (&o)[kAttnQG][D / 32], float (&l_run)[kAttnQG], int& ev_cur, int* s_next, int* ctr, int xcd, int per,
+    int64_t total, int fut, int& look) {
+  constexpr int QG = kAttnQG;
+  constexpr int KD = D / 16;
+  constexpr int DB = D / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hi = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int bh = it.bh;
+  const int64_t t0 = it.t0;
+  const int nkv = it.nkv;
+  const u16* kbase = it.kbase;
+  const u16* vtbase = it.vtbase;
   const int nt = (nkv + BN - 1) / BN;
   const float c = a.c;
 
-  f32x16 o[QG][DB];
-  f32x16 nm[QG];  // -m, the running maximum (log2 units), in all 16 registers
-  float l_run[QG];
+  f16x8 qf[QG][KD];
+  int eq[QG];         // per query row: operands carry q * log2(e)/sqrt(D) * 2^-eq
+  float lsc = 1.0f;   // 2^-d of the tile whose P is turned next (scaled loop)
+  f32x16 nm[QG];      // -m, the running maximum (log2 units), in all 16 registers
+  ev_cur = 0;         // V^T unit: O holds O_true * 2^-ev_cur (scaled loop)
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     l_run[g] = 0.0f;
@@ -908,11 +979,6 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   // score moves the maximum between the two phases (rare).  K tile j+1 and
   // V tile j are resident during step j; K tile
   // j+2 and V tile j+1 stream into the other stages meanwhile.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // the buffer resources below need wave-uniform bases and sizes
-  kbase = uniform_ptr(kbase);
-  vtbase = uniform_ptr(vtbase);
-  nkv = __builtin_amdgcn_readfirstlane(nkv);
   // The scaled variant (SC) handles nonzero exponents: its score
   // accumulators start from zero, so a tile's raw scores are
   // s * 2^-(eq + ek); after phase B they are moved to s - m in fp32 for the
@@ -1031,12 +1097,8 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   // computes, then waits for its own DMAs and syncs.  No DMA is outstanding
   // at a branch merge; the last half-iteration re-loads clamped tiles instead
   // of branching around the DMA, and its scores of the tile past the end are
-  // never used.
+  // never used.  The item's first three tile DMAs are already in flight.
   f32x16 sa[QG][2], sb[QG][2];
-  issue_k<D>(ks0, 0, tid, wave_u, nkv, kbase);
-  issue_v<D>(vt0, 0, tid, wave_u, vtbase);
-  issue_k<D>(ks1, min(1, nt - 1), tid, wave_u, nkv, kbase);
-  __builtin_amdgcn_sched_barrier(0);  // all three DMAs before the rotation's waits
   // Each query row carries its own power-of-two exponent eq (operand_exponent
   // of the row's largest turned and scaled magnitude, the two lanes of a
   // query column agreeing); a row with eq != 0 is converted again at
@@ -1047,25 +1109,31 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
     float mx = 0.0f;
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qf[g][kd] = __builtin_bit_cast(f16x8, rope8_f16_max(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c, mx));
-    eq[g] = operand_exponent(pair_max(qvalid[g] ? mx : 0.0f));
+      qf[g][kd] =
+          __builtin_bit_cast(f16x8, rope8_f16_max(qs.qraw[g][kd], qs.qcs[g][kd][0], qs.qcs[g][kd][1], c, mx));
+    eq[g] = operand_exponent(pair_max(qs.qvalid[g] ? mx : 0.0f));
     if (eq[g] != 0) {
       any_eq = true;
 #pragma unroll
       for (int kd = 0; kd < KD; ++kd)
-        qf[g][kd] =
-            __builtin_bit_cast(f16x8, rope8_f16_max(qraw[g][kd], qcs[g][kd][0], qcs[g][kd][1], c, mx, eq[g]));
+        qf[g][kd] = __builtin_bit_cast(
+            f16x8, rope8_f16_max(qs.qraw[g][kd], qs.qcs[g][kd][0], qs.qcs[g][kd][1], c, mx, eq[g]));
     }
   }
   // An item runs the scaled loop when a query row or a key or value tile of
   // its (batch, head) carries a nonzero exponent; the plain kernel lists
-  // such an item for the scaled kernel and ends once its DMAs have landed.
+  // such an item for the scaled kernel and moves on once its DMAs have
+  // landed.  The same barrier publishes the next item's id.
   constexpr bool scaled = SCALED;
   if constexpr (!SCALED) {
-    if (__syncthreads_or(any_eq ? 1 : 0) || a.flags[bh] != 0) {
-      if (tid == 0) a.redo[1 + atomicAdd(a.redo, 1)] = (int)L;
+    if (tid == 0) *s_next = claim_from(ctr, xcd, per, total, fut);
+    const bool hand_off = __syncthreads_or(any_eq ? 1 : 0) || a.flags[bh] != 0;
+    look = __builtin_amdgcn_readfirstlane(*s_next);
+    if (hand_off) {
+      if (tid == 0) a.redo[1 + atomicAdd(a.redo, 1)] = it.L;
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      return;
+      __syncthreads();  // every wave has read s_next before it is written again
+      return true;
     }
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
@@ -1073,7 +1141,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   if constexpr (scaled) {
     tile_scores<D, QG>(sa, ks0, n, hi, qf);
     // raw scores are s * 2^-(eq + ek); the first tile also fixes the V unit
-    const int64_t eb = bh * a.k_tiles + t0;
+    const int64_t eb = (int64_t)bh * a.k_tiles + t0;
     const int ek0 = a.kexp[eb];
     ev_cur = a.vexp[eb];
 #pragma unroll
@@ -1107,7 +1175,7 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   __syncthreads();
   bool any_q = false;
 #pragma unroll
-  for (int g = 0; g < QG; ++g) any_q |= qvalid[g];
+  for (int g = 0; g < QG; ++g) any_q |= qs.qvalid[g];
   if (__any(any_q)) {
     if constexpr (!scaled) {
       for (int j = 0; j < nt; j += 2) {
@@ -1143,7 +1211,22 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
     }
   }
 
-  // ---- epilogue: normalise and write
+  return false;
+}
+
+// Normalises the item's outputs and writes them: bf16 rows for tokens one
+// window covers (and every dense query), fp32 blend slots for the others.
+template <int D, bool WIN>
+__device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a, const Item& it,
+                                                               const int (&qtok)[kAttnQG],
+                                                               const bool (&qvalid)[kAttnQG],
+                                                               f32x16 (&o)[kAttnQG][D / 32],
+                                                               float (&l_run)[kAttnQG], int ev_cur) {
+  constexpr int QG = kAttnQG, BM = kAttnBM, DB = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, hi = lane >> 5;
+  const int64_t bh = it.bh;
+  const int qtile = it.qtile, rec = it.rec, qh = it.qh, qw = it.qw;
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     float lt = pair_sum(l_run[g]);
@@ -1188,8 +1271,11 @@ __device__ __attribute__((always_inline)) inline void attn_item(const AttnArgs& 
   }
 }
 
-// The plain kernel: one work item per work-group, logical ids contiguous
-// per XCD (consecutive items share a window's keys in one L2).
+// The plain kernel: persistent work-groups, one per CU, claim work items
+// from per-XCD counters (logical ids contiguous per XCD, so consecutive
+// items of a window share its keys in one L2).  After an item's last tile,
+// the next item's first tile DMAs are issued before the item's epilogue, so
+// their latency overlaps it and no work-group launch separates the items.
 template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const AttnArgs a) {
   // two LDS stages, as separate objects so that the compiler can tell a DMA
@@ -1198,9 +1284,49 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   __shared__ __attribute__((aligned(16))) u16 vt0[D * BN];
   __shared__ __attribute__((aligned(16))) u16 ks1[BN * D];
   __shared__ __attribute__((aligned(16))) u16 vt1[D * BN];
-  const int pid = blockIdx.x;
-  const int64_t L = (int64_t)(pid & 7) * (a.grid >> 3) + (pid >> 3);
-  attn_item<D, WIN, false>(a, L, ks0, vt0, ks1, vt1);
+  __shared__ int s_next;
+  const int tid = threadIdx.x;
+  const int xcd = blockIdx.x & 7;
+  // logical ids: (batch, head)-major over the call's items, split into 8
+  // contiguous shares, one per XCD
+  const int64_t total = (WIN ? (int64_t)a.n_items[0] : (int64_t)a.n_qtiles) * a.BH;
+  const int per = (int)((total + 7) >> 3);
+  int* ctr = a.ctr;
+  if (tid == 0) s_next = claim_from(ctr, xcd, per, total, atomicAdd(&ctr[xcd], 1));
+  __syncthreads();
+  const int first = __builtin_amdgcn_readfirstlane(s_next);
+  __syncthreads();
+  if (first < 0) return;
+  // pre: the item's first tile DMAs are already in flight at the loop head.
+  // Its query loads wait for the loop head: kept in registers across the
+  // epilogue they would crowd the key loop's registers.
+  int cur = first;
+  bool pre = false;
+  while (cur >= 0) {
+    const Item it = decode_item<D, WIN>(a, cur);
+    Queries<D> qs;
+    load_queries<D, WIN>(a, it, qs);
+    if (!pre) issue_first<D>(it, ks0, vt0, ks1);
+    __builtin_amdgcn_sched_barrier(0);  // the DMAs before the rotation's waits
+    int fut = 0;
+    if (tid == 0) fut = atomicAdd(&ctr[xcd], 1);  // the next item, resolved at the item's first barrier
+    f32x16 o[kAttnQG][D / 32];
+    float l_run[kAttnQG];
+    int ev_cur = 0, look = -1;
+    const bool listed = compute_item<D, WIN, false>(a, it, qs, ks0, vt0, ks1, vt1, o, l_run, ev_cur, &s_next, ctr,
+                                                    xcd, per, total, fut, look);
+    pre = false;
+    if (!listed) {
+      // every LDS stage is free once the key loop's last barrier is passed
+      if (look >= 0) {
+        issue_first<D>(decode_item<D, WIN>(a, look), ks0, vt0, ks1);
+        pre = true;
+      }
+      epilogue<D, WIN>(a, it, qs.qtok, qs.qvalid, o, l_run, ev_cur);
+    }
+    cur = look;
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
 
 // The scaled kernel: work-groups walk the items the plain kernel listed
@@ -1213,7 +1339,17 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_scaled_kernel
   __shared__ __attribute__((aligned(16))) u16 vt1[D * BN];
   const int cnt = a.redo[0];
   for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
-    attn_item<D, WIN, true>(a, a.redo[1 + i], ks0, vt0, ks1, vt1);
+    const Item it = decode_item<D, WIN>(a, a.redo[1 + i]);
+    Queries<D> qs;
+    load_queries<D, WIN>(a, it, qs);
+    issue_first<D>(it, ks0, vt0, ks1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 o[kAttnQG][D / 32];
+    float l_run[kAttnQG];
+    int ev_cur = 0, look = -1;
+    compute_item<D, WIN, true>(a, it, qs, ks0, vt0, ks1, vt1, o, l_run, ev_cur, nullptr, nullptr, 0, 0, 0, 0,
+                               look);
+    epilogue<D, WIN>(a, it, qs.qtok, qs.qvalid, o, l_run, ev_cur);
     __syncthreads();
   }
 }
@@ -1306,16 +1442,31 @@ __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* 
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+    cus[dev] = n / 8 * 8;
+  }
+  return cus[dev];
+}
+
+// work: an upper bound of the call's work items (the window plan's count is
+// on the device).
 template <bool WIN>
 int launch_attn(const AttnArgs& a, int D, int64_t work, hipStream_t st) {
-  AttnArgs b = a;
-  int64_t g = (work + 7) / 8 * 8;
-  if (g > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "attention grid too large");
-  b.grid = (int)g;
-  dim3 grid((unsigned)b.grid);
+  const AttnArgs& b = a;
+  if (work > 0x7FFFFFF0LL) return fail(AREA_E_UNSUPPORTED, "attention work too large");
+  const int64_t g = (work + 7) / 8 * 8;
+  // the plain kernel is persistent: one work-group per CU slot
+  dim3 grid((unsigned)std::min<int64_t>(g, (int64_t)device_cus() * kAttnGroupsPerCu));
   // the scaled kernel's work-groups walk the listed items, one work-group
   // per CU (the register budget of one fits a CU)
-  dim3 grid_scaled((unsigned)std::min<int64_t>(g, 256));
+  dim3 grid_scaled((unsigned)std::min<int64_t>(g, device_cus()));
   AttnEvents ev = attn_events();
   if (ev.begin) {
     hipError_t e = hipEventRecord((hipEvent_t)ev.begin, st);
@@ -1386,7 +1537,8 @@ int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int G
   a.kexp = kexp;
   a.vexp = vexp;
   a.flags = flags;
-  a.redo = flags + BH;
+  a.ctr = flags + BH;
+  a.redo = flags + BH + 8;
   a.n_kv = Nk;
   a.n_qtiles = (Nq + kAttnBM - 1) / kAttnBM;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)D));
@@ -1444,7 +1596,8 @@ int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32
   a.kexp = ws.kexp;
   a.vexp = ws.vexp;
   a.flags = ws.flags;
-  a.redo = ws.flags + w.BH;
+  a.ctr = ws.flags + w.BH;
+  a.redo = ws.flags + w.BH + 8;
   a.c = (float)(1.4426950408889634 / std::sqrt((double)w.D));
   a.plan = plan;
   a.wsum = wsum;

@@ -124,12 +124,13 @@ def test_gated_canvas_keeps_full_attention():
     # fp16 key rows and V^T tiles (N is a multiple of 64), the two layouts of
     # the (cos, sin) table of 64 positions x D/4 frequencies, one exponent per
     # (head, 64-key tile) for K and for V, and the range words (a flag per
-    # head, the scaled-item count and list of up to N/256 items per head),
+    # head, 8 work counters, the scaled-item count and list of up to N/256
+    # items per head),
     # each region rounded up to 256 bytes
     up = lambda x: (x + 255) // 256 * 256
     BH, tiles = p.B * p.H, p.N // 64
     expect = (2 * BH * p.N * p.D * 2 + 2 * 64 * (p.D // 4) * 8 + 2 * up(BH * tiles * 4)
-              + up((BH + 1 + BH * (p.N // 256)) * 4))
+              + up((BH + 9 + BH * (p.N // 256)) * 4))
     assert A.area_workspace_bytes(p, A.OP_FULL) == expect
 
 
@@ -189,7 +190,7 @@ def test_workspace_sizes():
     tok = BH * p.N * p.D * 2
     tab = 2 * max(p.Gh, p.Gw) * (p.D // 4) * 8                 # (cos, sin) tables
     exps = 2 * up(BH * (p.N // 64) * 4)                        # per-tile exponents of K and V
-    words = up((BH + 1 + BH * (p.N // 256)) * 4)               # range flags, scaled-item list
+    words = up((BH + 9 + BH * (p.N // 256)) * 4)               # range flags, scaled-item list
     # fp16 key rows + V^T tiles + tables + exponents + range words; coarse
     # attention has the same layout (pooled keys down to f = 1)
     assert A.area_workspace_bytes(p, A.OP_FULL) == 2 * tok + tab + exps + words
