@@ -862,24 +862,42 @@ struct Queries {
   float4 qcs[kAttnQG][D / 16][2];
 };
 
-template <int D, bool WIN>
-__device__ __attribute__((always_inline)) inline void load_queries(const AttnArgs& a, const Item& it,
-                                                                   Queries<D>& q) {
-  constexpr int QG = kAttnQG, BM = kAttnBM, KD = D / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 31, hi = lane >> 5;
+// The lane's query token rows in the item and their validity.  Each call
+// rebuilds them from the item, so that nothing lane-derived has to survive
+// the key loop.
+template <bool WIN>
+__device__ __attribute__((always_inline)) inline void query_tokens(const AttnArgs& a, const Item& it,
+                                                                   int (&qtok)[kAttnQG], bool (&qvalid)[kAttnQG]) {
+  constexpr int QG = kAttnQG, BM = kAttnBM;
+  const int tid = (int)threadIdx.x;
+  const int n = tid & 31, wave = tid >> 6;
+  // the grid width behind an empty asm: its division reciprocal is formed
+  // per item, not held across the key loop
+  int gw = a.Gw;
+  asm volatile("" : "+s"(gw));
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     const int t = it.qtile * BM + wave * 32 * QG + 32 * g + n;
-    q.qvalid[g] = t < it.nq;
+    qvalid[g] = t < it.nq;
     if constexpr (WIN) {
-      const int yy = q.qvalid[g] ? t / it.qw : 0;
-      const int xx = q.qvalid[g] ? t - yy * it.qw : 0;
-      q.qtok[g] = (it.qy0 + yy) * a.Gw + it.qx0 + xx;
+      const int yy = qvalid[g] ? t / it.qw : 0;
+      const int xx = qvalid[g] ? t - yy * it.qw : 0;
+      qtok[g] = (it.qy0 + yy) * gw + it.qx0 + xx;
     } else {
-      q.qtok[g] = q.qvalid[g] ? t : 0;
+      qtok[g] = qvalid[g] ? t : 0;
     }
   }
+}
+
+template <int D, bool WIN>
+__device__ __attribute__((always_inline)) inline void load_queries(const AttnArgs& a, const Item& it,
+                                                                   Queries<D>& q) {
+  constexpr int QG = kAttnQG, KD = D / 16;
+  const int tid = (int)threadIdx.x;
+  const int hi = (tid & 63) >> 5;
+  int gw = a.Gw;
+  asm volatile("" : "+s"(gw));
+  query_tokens<WIN>(a, it, q.qtok, q.qvalid);
   // MFMA B operand: chunk 2 kd + hi (channels 16 kd + 8 hi ..) of the
   // lane's query, turned by RoPE at its grid position (chunks of the first
   // half follow the row, the others the column; text rows sit at (0, 0)).
@@ -889,8 +907,8 @@ __device__ __attribute__((always_inline)) inline void load_queries(const AttnArg
     int py = 0, px = 0;
     if (row >= a.q_text) {
       const int img = (int)(row - a.q_text);
-      py = img / a.Gw;
-      px = img - py * a.Gw;
+      py = img / gw;
+      px = img - py * gw;
     }
     const u32x4* qrow = reinterpret_cast<const u32x4*>(it.qbase + (int64_t)q.qtok[g] * D);
 #pragma unroll
@@ -910,7 +928,7 @@ __device__ __attribute__((always_inline)) inline void load_queries(const AttnArg
 // tile 1 (or 0 again) into stage 1.
 template <int D>
 __device__ __attribute__((always_inline)) inline void issue_first(const Item& it, u16* ks0, u16* vt0, u16* ks1) {
-  const int tid = threadIdx.x;
+  const int tid = (int)threadIdx.x;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = (it.nkv + BN - 1) / BN;
   issue_k<D>(ks0, 0, tid, wave_u, it.nkv, it.kbase);
@@ -938,16 +956,17 @@ __device__ inline int claim_from(int* ctr, int xcd, int per, int64_t total, int 
 // scaled loop (the plain kernel lists it and returns true), the first tile's
 // scores and the software-pipelined loop over the key tiles.  The plain
 // kernel also resolves the next item here: `fut` (thread 0's draw from its
-// XCD's counter) becomes `look`, shared through s_next.
+// XCD's counter) becomes `look`.  s_sync: kAttnWaves + 1 LDS words (the
+// waves' votes, then the next item's id).
 template <int D, bool WIN, bool SCALED>
 __device__ __attribute__((always_inline)) inline bool compute_item(
     const AttnArgs& a, const Item& it, Queries<D>& qs, u16* ks0, u16* vt0, u16* ks1, u16* vt1,
-    f32x16 (&o)[kAttnQG][D / 32], float (&l_run)[kAttnQG], int& ev_cur, int* s_next, int* ctr, int xcd, int per,
+    f32x16 (&o)[kAttnQG][D / 32], float (&l_run)[kAttnQG], int& ev_cur, int* s_sync, int* ctr, int xcd, int per,
     int64_t total, int fut, int& look) {
   constexpr int QG = kAttnQG;
   constexpr int KD = D / 16;
   constexpr int DB = D / 32;
-  const int tid = threadIdx.x;
+  const int tid = (int)threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hi = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -1126,13 +1145,21 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
   // landed.  The same barrier publishes the next item's id.
   constexpr bool scaled = SCALED;
   if constexpr (!SCALED) {
-    if (tid == 0) *s_next = claim_from(ctr, xcd, per, total, fut);
-    const bool hand_off = __syncthreads_or(any_eq ? 1 : 0) || a.flags[bh] != 0;
-    look = __builtin_amdgcn_readfirstlane(*s_next);
+    // a work-group vote: each wave posts whether any of its rows has an
+    // exponent (every wave writes its word, so none needs clearing)
+    const bool wave_eq = __ballot(any_eq ? 1 : 0) != 0;
+    if (lane == 0) s_sync[wave] = wave_eq ? 1 : 0;
+    if (tid == 0) s_sync[kAttnWaves] = claim_from(ctr, xcd, per, total, fut);
+    __syncthreads();
+    int votes = 0;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) votes |= s_sync[w];
+    const bool hand_off = votes != 0 || a.flags[bh] != 0;
+    look = __builtin_amdgcn_readfirstlane(s_sync[kAttnWaves]);
     if (hand_off) {
       if (tid == 0) a.redo[1 + atomicAdd(a.redo, 1)] = it.L;
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
-      __syncthreads();  // every wave has read s_next before it is written again
+      __syncthreads();  // every wave has read s_sync before it is written again
       return true;
     }
   }
@@ -1218,12 +1245,14 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
 // window covers (and every dense query), fp32 blend slots for the others.
 template <int D, bool WIN>
 __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a, const Item& it,
-                                                               const int (&qtok)[kAttnQG],
-                                                               const bool (&qvalid)[kAttnQG],
                                                                f32x16 (&o)[kAttnQG][D / 32],
                                                                float (&l_run)[kAttnQG], int ev_cur) {
   constexpr int QG = kAttnQG, BM = kAttnBM, DB = D / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int qtok[QG];
+  bool qvalid[QG];
+  query_tokens<WIN>(a, it, qtok, qvalid);
+  const int tid = (int)threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hi = lane >> 5;
   const int64_t bh = it.bh;
   const int qtile = it.qtile, rec = it.rec, qh = it.qh, qw = it.qw;
@@ -1232,10 +1261,7 @@ __device__ __attribute__((always_inline)) inline void epilogue(const AttnArgs& a
     float lt = pair_sum(l_run[g]);
     float inv = ldexpf(1.0f / lt, ev_cur);
     if (!qvalid[g]) continue;
-    // an opaque copy of the query's row: its addresses are recomputed here
-    // rather than kept live in registers across the key loop
-    int qt = qtok[g];
-    asm volatile("" : "+v"(qt));
+    const int qt = qtok[g];
     bool direct = true;
     int t = 0;
     if constexpr (WIN) {
@@ -1284,17 +1310,16 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
   __shared__ __attribute__((aligned(16))) u16 vt0[D * BN];
   __shared__ __attribute__((aligned(16))) u16 ks1[BN * D];
   __shared__ __attribute__((aligned(16))) u16 vt1[D * BN];
-  __shared__ int s_next;
-  const int tid = threadIdx.x;
+  __shared__ int s_sync[kAttnWaves + 1];
   const int xcd = blockIdx.x & 7;
   // logical ids: (batch, head)-major over the call's items, split into 8
   // contiguous shares, one per XCD
   const int64_t total = (WIN ? (int64_t)a.n_items[0] : (int64_t)a.n_qtiles) * a.BH;
   const int per = (int)((total + 7) >> 3);
   int* ctr = a.ctr;
-  if (tid == 0) s_next = claim_from(ctr, xcd, per, total, atomicAdd(&ctr[xcd], 1));
+  if (threadIdx.x == 0) s_sync[kAttnWaves] = claim_from(ctr, xcd, per, total, atomicAdd(&ctr[xcd], 1));
   __syncthreads();
-  const int first = __builtin_amdgcn_readfirstlane(s_next);
+  const int first = __builtin_amdgcn_readfirstlane(s_sync[kAttnWaves]);
   __syncthreads();
   if (first < 0) return;
   // pre: the item's first tile DMAs are already in flight at the loop head.
@@ -1309,11 +1334,11 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
     if (!pre) issue_first<D>(it, ks0, vt0, ks1);
     __builtin_amdgcn_sched_barrier(0);  // the DMAs before the rotation's waits
     int fut = 0;
-    if (tid == 0) fut = atomicAdd(&ctr[xcd], 1);  // the next item, resolved at the item's first barrier
+    if ((int)threadIdx.x == 0) fut = atomicAdd(&ctr[xcd], 1);  // the next item, resolved at the item's first barrier
     f32x16 o[kAttnQG][D / 32];
     float l_run[kAttnQG];
     int ev_cur = 0, look = -1;
-    const bool listed = compute_item<D, WIN, false>(a, it, qs, ks0, vt0, ks1, vt1, o, l_run, ev_cur, &s_next, ctr,
+    const bool listed = compute_item<D, WIN, false>(a, it, qs, ks0, vt0, ks1, vt1, o, l_run, ev_cur, s_sync, ctr,
                                                     xcd, per, total, fut, look);
     pre = false;
     if (!listed) {
@@ -1322,7 +1347,7 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_kernel(const 
         issue_first<D>(decode_item<D, WIN>(a, look), ks0, vt0, ks1);
         pre = true;
       }
-      epilogue<D, WIN>(a, it, qs.qtok, qs.qvalid, o, l_run, ev_cur);
+      epilogue<D, WIN>(a, it, o, l_run, ev_cur);
     }
     cur = look;
   }
@@ -1349,7 +1374,7 @@ __global__ __launch_bounds__(kThreads, kAttnGroupsPerCu) void attn_scaled_kernel
     int ev_cur = 0, look = -1;
     compute_item<D, WIN, true>(a, it, qs, ks0, vt0, ks1, vt1, o, l_run, ev_cur, nullptr, nullptr, 0, 0, 0, 0,
                                look);
-    epilogue<D, WIN>(a, it, qs.qtok, qs.qvalid, o, l_run, ev_cur);
+    epilogue<D, WIN>(a, it, o, l_run, ev_cur);
     __syncthreads();
   }
 }
