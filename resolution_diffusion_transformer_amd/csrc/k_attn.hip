@@ -1388,82 +1388,140 @@ struct BlendArgs {
 };
 
 constexpr int kBlendTok = 16;
+constexpr int kBlendBatch = 4;  // elements per lane whose slot loads are in flight together
 constexpr int kMaxCover = 8;
 
 __device__ inline int tent_w(int u, int L) { return min(u + 1, L - u); }
 
 // Tokens covered by more than one window: out = sum_w wt_w * O_w / wsum,
-// windows in record order.  One block per kBlendTok tokens: the first
-// kBlendTok threads find their token's covering windows in parallel, then
-// the whole block writes the blended rows of the overlapped ones.
+// windows in record order.  One block per kBlendTok tokens: the window
+// positions are staged in LDS, the first kBlendTok threads find their
+// token's covering rows and columns of windows, then kBlendTok threads per
+// token look up one covering window each (its record, quadrant, slot and
+// tent weight); finally each wave blends the block's overlapped tokens in
+// turn.
 __global__ __launch_bounds__(256) void blend_kernel(BlendArgs b, const int32_t* __restrict__ plan,
                                                     const int* __restrict__ rec_start, const int* __restrict__ slot_off,
                                                     const int32_t* __restrict__ wsum, const float* __restrict__ slots,
                                                     u16* __restrict__ out) {
+  static_assert(kBlendTok * kBlendTok == 256, "one looker-up per (token, covering window) slot");
+  __shared__ int s_ys[kMaxAxisWindows], s_xs[kMaxAxisWindows];
   __shared__ int s_slot[kBlendTok][kMaxCover * kMaxCover];
   __shared__ float s_wt[kBlendTok][kMaxCover * kMaxCover];
   __shared__ int s_cnt[kBlendTok];
+  __shared__ int s_cover[kBlendTok][4];  // first covering row window, their count; the same for columns
+  __shared__ int s_list[kBlendTok];      // the block's tokens that more than one window covers
+  __shared__ int s_nov;
   const int64_t N = (int64_t)b.Gh * b.Gw;
   const int64_t p0 = (int64_t)blockIdx.x * kBlendTok;
-  if (threadIdx.x < kBlendTok) {
-    const int t = threadIdx.x;
-    const int64_t p = p0 + t;
-    int cnt = 0;
+  const int tid = threadIdx.x;
+  if (tid < b.ny) s_ys[tid] = b.ys[tid];
+  if (tid >= kMaxAxisWindows && tid - kMaxAxisWindows < b.nx) s_xs[tid - kMaxAxisWindows] = b.xs[tid - kMaxAxisWindows];
+  __syncthreads();
+  if (tid < kBlendTok) {
+    const int64_t p = p0 + tid;
+    int i0 = 0, cy = 0, j0 = 0, cx = 0;
     if (p < N) {
-      const int y = (int)(p / b.Gw), x = (int)(p % b.Gw);
-      int iy[kMaxCover], ix[kMaxCover], cy = 0, cx = 0;
+      // window starts along an axis never decrease and all windows of an
+      // axis have one length, so a token's covering windows on that axis
+      // are consecutive; the first kMaxCover of them are kept
+      const int y = (int)p / b.Gw, x = (int)p % b.Gw;
       for (int i = 0; i < b.ny; ++i)
-        if (y >= b.ys[i] && y < b.ys[i] + b.Ly && cy < kMaxCover) iy[cy++] = i;
+        if (y >= s_ys[i] && y < s_ys[i] + b.Ly && cy < kMaxCover) {
+          if (cy == 0) i0 = i;
+          ++cy;
+        }
       for (int j = 0; j < b.nx; ++j)
-        if (x >= b.xs[j] && x < b.xs[j] + b.Lx && cx < kMaxCover) ix[cx++] = j;
-      if (cy * cx > 1) {
-        for (int a = 0; a < cy; ++a)
-          for (int c = 0; c < cx; ++c) {
-            int r0 = rec_start[iy[a] * b.nx + ix[c]];
-            int rr = r0;
-            const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * r0;
-            if (rp[9] >= 0) {
-              // split window: pick the quadrant holding (y, x)
-              for (int qd = 0; qd < 4; ++qd) {
-                const int32_t* qp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * (r0 + qd);
-                if (y >= qp[0] && y < qp[0] + qp[2] && x >= qp[1] && x < qp[1] + qp[3]) rr = r0 + qd;
-              }
-            }
-            const int32_t* wp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rr;
-            int uy = y - wp[0], ux = x - wp[1];
-            s_wt[t][cnt] = (float)(tent_w(uy, wp[2]) * tent_w(ux, wp[3]));
-            s_slot[t][cnt] = slot_off[rr] + uy * wp[3] + ux;
-            ++cnt;
-          }
-      }
+        if (x >= s_xs[j] && x < s_xs[j] + b.Lx && cx < kMaxCover) {
+          if (cx == 0) j0 = j;
+          ++cx;
+        }
     }
-    s_cnt[t] = cnt;
+    s_cover[tid][0] = i0;
+    s_cover[tid][1] = cy;
+    s_cover[tid][2] = j0;
+    s_cover[tid][3] = cx;
+    s_cnt[tid] = cy * cx > 1 ? cy * cx : 0;
   }
   __syncthreads();
-  const int D4 = b.D / 4;
-  const int64_t per_tok = b.BH * D4;
-  for (int64_t e = threadIdx.x; e < kBlendTok * per_tok; e += blockDim.x) {
-    const int t = (int)(e / per_tok);
+  {
+    const int t = tid / kBlendTok;
+    const int64_t p = p0 + t;
     const int cnt = s_cnt[t];
-    if (cnt <= 1) continue;
-    const int64_t r = e - t * per_tok;
-    const int64_t bh = r / D4;
-    const int d4 = (int)(r - bh * D4);
+    const int i0 = s_cover[t][0], j0 = s_cover[t][2], cx = s_cover[t][3];
+    for (int k = tid % kBlendTok; k < cnt; k += kBlendTok) {
+      const int y = (int)p / b.Gw, x = (int)p % b.Gw;
+      const int r0 = rec_start[(i0 + k / cx) * b.nx + j0 + k % cx];
+      int rr = r0;
+      const int32_t* rp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * r0;
+      if (rp[9] >= 0) {
+        // split window: pick the quadrant holding (y, x)
+        for (int qd = 0; qd < 4; ++qd) {
+          const int32_t* qp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * (r0 + qd);
+          if (y >= qp[0] && y < qp[0] + qp[2] && x >= qp[1] && x < qp[1] + qp[3]) rr = r0 + qd;
+        }
+      }
+      const int32_t* wp = plan + AREA_PLAN_HEADER + AREA_PLAN_REC * rr;
+      const int uy = y - wp[0], ux = x - wp[1];
+      s_wt[t][k] = (float)(tent_w(uy, wp[2]) * tent_w(ux, wp[3]));
+      s_slot[t][k] = slot_off[rr] + uy * wp[3] + ux;
+    }
+  }
+  if (tid == 0) {
+    int n = 0;
+    for (int t = 0; t < kBlendTok; ++t)
+      if (s_cnt[t] > 1) s_list[n++] = t;
+    s_nov = n;
+  }
+  __syncthreads();
+  // Each wave takes the block's overlapped tokens in turn; per token, the
+  // (batch*head, 4 channels) elements in batches of kBlendBatch per lane,
+  // all of a batch's slot loads in flight together.  32-bit index
+  // arithmetic: D/4 is a power of two and BH * D/4 fits an int (checked by
+  // the host).
+  const int d4_bits = b.D == 128 ? 5 : 4;
+  const int per_tok = (int)b.BH << d4_bits;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int q = wave; q < s_nov; q += 256 / 64) {
+    const int t = s_list[q];
+    const int cnt = s_cnt[t];
     const int64_t p = p0 + t;
     const float inv = 1.0f / (float)wsum[p];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i = 0; i < cnt; ++i) {
-      float4 v = *reinterpret_cast<const float4*>(slots + ((int64_t)s_slot[t][i] * b.BH + bh) * b.D + 4 * d4);
-      float wgt = s_wt[t][i];
-      acc.x += wgt * v.x;
-      acc.y += wgt * v.y;
-      acc.z += wgt * v.z;
-      acc.w += wgt * v.w;
+    for (int r0 = lane; r0 < per_tok; r0 += 64 * kBlendBatch) {
+      float4 acc[kBlendBatch];
+#pragma unroll
+      for (int k = 0; k < kBlendBatch; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int i = 0; i < cnt; ++i) {
+        const float wgt = s_wt[t][i];
+        const float* base = slots + (int64_t)s_slot[t][i] * b.BH * b.D;
+        float4 v[kBlendBatch];
+#pragma unroll
+        for (int k = 0; k < kBlendBatch; ++k) {
+          const int r = r0 + 64 * k;
+          v[k] = r < per_tok ? *reinterpret_cast<const float4*>(base + ((int64_t)(r >> d4_bits) * b.D +
+                                                                        4 * (r & ((1 << d4_bits) - 1))))
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < kBlendBatch; ++k) {
+          acc[k].x += wgt * v[k].x;
+          acc[k].y += wgt * v[k].y;
+          acc[k].z += wgt * v[k].z;
+          acc[k].w += wgt * v[k].w;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBlendBatch; ++k) {
+        const int r = r0 + 64 * k;
+        if (r >= per_tok) continue;
+        const int bh = r >> d4_bits;
+        const int c4 = 4 * (r & ((1 << d4_bits) - 1));
+        uint2 pk;
+        pk.x = (unsigned)f2bf(acc[k].x * inv) | ((unsigned)f2bf(acc[k].y * inv) << 16);
+        pk.y = (unsigned)f2bf(acc[k].z * inv) | ((unsigned)f2bf(acc[k].w * inv) << 16);
+        *reinterpret_cast<uint2*>(out + ((int64_t)bh * (N + b.T) + b.T + p) * b.D + c4) = pk;
+      }
     }
-    uint2 pk;
-    pk.x = (unsigned)f2bf(acc.x * inv) | ((unsigned)f2bf(acc.y * inv) << 16);
-    pk.y = (unsigned)f2bf(acc.z * inv) | ((unsigned)f2bf(acc.w * inv) << 16);
-    *reinterpret_cast<uint2*>(out + (bh * (N + b.T) + b.T + p) * b.D + 4 * d4) = pk;
   }
 }
 
@@ -1574,6 +1632,8 @@ int launch_dense_attn(const void* q, const void* rope, int q_text, int Gh, int G
 int launch_window_attn(const WindowAttnArgs& w, const int32_t* plan, const int32_t* wsum, const int32_t* bridge_idx,
                        const void* q, const void* k, const void* v, const void* rope, void* out, const WindowWs& ws,
                        stream_t s) {
+  // the blend indexes (batch*head, 4 channels) in 32 bits
+  if (w.BH * (w.D / 4) > 0x7FFFFFFFLL) return fail(AREA_E_UNSUPPORTED, "blend: batch * heads too large");
   hipStream_t st = (hipStream_t)s;
   int n_base = w.ny * w.nx;
   const int R = bridge_idx ? w.R : 0;
