@@ -267,8 +267,9 @@ int area_pool_kv(const area_problem* p, int f, const void* k, const void* v,
 int area_coarse_attn(const area_problem* p, int f, const void* q, const void* kp,
                      const void* vp, void* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Haar detail map (ai.info summary, Methodology, Phase II: a DWT map of the
- * current state measures fine detail).  latent: [C][Gh][Gw] fp32.  For each
+/* Haar detail map (ai.info summary, Methodology, Phase II: a wavelet map of
+ * the hidden state gauges how much fine detail each region holds).
+ * latent: [C][Gh][Gw] fp32.  For each
  * 2x2 cell (a b / c d) and channel: LH = (a-b+c-d)/2, HL = (a+b-c-d)/2,
  * HH = (a-b-c+d)/2, summed in float64 as E += (LH^2 + HL^2) + HH^2 in
  * channel order.  energy: [Gh/2][Gw/2] fp32 (E rounded); energy_q:

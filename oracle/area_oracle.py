@@ -417,8 +417,8 @@ def axis_windows(G: int, w: int, seed: int, step: int, axis: int) -> Tuple[List[
 def detail_energy(latent: np.ndarray) -> np.ndarray:
     """READING R10: single-level orthonormal 2-D Haar transform per channel
     on 2x2 blocks (a b / c d) of the latent on the token grid ([summary]
-    Phase II: a DWT map of the current state measures fine detail; [readme]
-    Phase II bullet).  Detail energy per 2x2 cell:
+    Phase II: a wavelet map of the hidden state gauges how much fine detail
+    each region holds; [readme] Phase II bullet).  Detail energy per 2x2 cell:
         E = sum over channels (in order) of ((LH^2 + HL^2) + HH^2)
     with LH = (a - b + c - d)/2, HL = (a + b - c - d)/2, HH = (a - b - c + d)/2.
     Float64, each operation in the order written."""
