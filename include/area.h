@@ -22,7 +22,8 @@
  * --------------------------------
  *  * Tensors are caller-owned, contiguous DEVICE buffers.  Q, K, V and the
  *    outputs are bfloat16 laid out [B][H][T+Gh*Gw][D] (token sequences,
- *    below); image token n sits at grid row y = n / Gw, column x = n % Gw.  Q and K are passed WITHOUT
+ *    below); image token n sits at grid row y = n / Gw, column x = n % Gw.
+ *    Q and K are passed WITHOUT
  *    rotary embedding: the library rotates them itself (two-axis RoPE: the
  *    first D/2 channels encode y, the last D/2 encode x, channel pair
  *    (2k, 2k+1) of an axis half turns by pos * theta^(-4k/D)).
@@ -47,14 +48,17 @@
  *    error it returns a negative status and launches nothing.  On success
  *    it only enqueues kernels on `stream` (a hipStream_t; NULL = the null
  *    stream) and returns without synchronising.  The computing calls
- *    (area_pool_kv through area_attn_step) allocate, clear and copy
- *    nothing, so a caller may capture them (a whole step included) into a
- *    HIP graph and replay it.  A failed launch returns
+ *    (area_pool_kv through area_attn_step) allocate and copy nothing and
+ *    clear words only with their own kernels (no hipMemset), so a caller
+ *    may capture them (a whole step included) into a HIP graph and replay
+ *    it.  A failed launch returns
  *    AREA_E_HIP.  area_last_error() gives a per-thread description of the
  *    last failure.
- *  * Calls are re-entrant: no global mutable state other than the
- *    thread-local error text.  Two calls that share an output or workspace
- *    buffer must be ordered by the caller (same stream or events).
+ *  * Calls are re-entrant.  The only process state is the thread-local
+ *    error text and measurement events, a per-device cache of the CU
+ *    count, and the per-device scratch of area_window_plan_static.  Two
+ *    calls that share an output or workspace buffer must be ordered by the
+ *    caller (same stream or events).
  */
 #ifndef AREA_H
 #define AREA_H
