@@ -358,6 +358,7 @@ def config_summary(wl, m, cpu):
         "window_kernel_frac": round(ph["window_kernel_tflops"] / PEAK_MFMA_TFLOPS, 4),
         "area_tflops": round(m["area_tflops"], 1), "area_frac": round(m["area_tflops"] / PEAK_MFMA_TFLOPS, 4),
         "pool_gbs": round(ph["pool_gbs"], 1), "pool_frac_hbm": round(ph["pool_gbs"] / PEAK_HBM_GBS, 4),
+        "per_step_ms": ph["per_step_ms"],
         "cpu_oracle": cpu,
     }
 
@@ -671,6 +672,7 @@ def cpu_baseline(wl, q, k, v, lat, sched, flops, win_pairs, full_flops, coarse_r
     full_ms = 1e3 * (H * t_fix + t_var * full_flops / (4.0 * D * max(len(r) - 1, 1) * N))
     ms_per_step = sum(est_ms.values()) / max(len(est_ms), 1)
     return {"value": round(ms_per_step, 1), "unit": "ms/step", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": (f"float64 NumPy oracle on head 0 of {H}: Phase I step at f0 ({min(coarse_rows, N)} query "
                        f"rows), Phase II steps 0, 1 and S-1 ({min(rows, N)} sampled query rows each, with the step's "
                        f"Haar map, plan and bridge), full attention ({min(full_rows, N)} rows); a one-row call gives "
@@ -682,6 +684,18 @@ def cpu_baseline(wl, q, k, v, lat, sched, flops, win_pairs, full_flops, coarse_r
             "full_attn_note": (f"head 0, {min(full_rows, N)} of {N} query rows timed, scaled to all rows and x{H} "
                                f"heads (extrapolated)"),
             "speedup_vs_full_oracle": round(full_ms / ms_per_step, 3) if ms_per_step > 0 else None}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
