@@ -4,11 +4,13 @@
 //
 // Design (CDNA4, wave64):
 //  * One attention kernel for every mode.  Its key/value set is always a
-//    contiguous run of fp16 K rows plus fp16 V^T tiles of 64 keys: full and
-//    coarse attention use the prepared tensors directly, windowed attention
-//    first gathers each window's keys (Halo rectangle, then the bridge tokens
-//    outside it, compacted; turned by RoPE on the way) with a bandwidth-bound
-//    kernel, so no index math or transposition remains in the MFMA loop.
+//    contiguous run of fp16 K rows plus fp16 V^T tiles of 64 keys, each tile
+//    with a power-of-two exponent: full and coarse attention convert their
+//    keys once per call (kv_tiles_kernel), windowed attention first gathers
+//    each window's keys (Halo rectangle, then the bridge tokens outside it,
+//    compacted, then the text keys; turned by RoPE on the way) with a
+//    bandwidth-bound kernel, so no index math or transposition remains in
+//    the MFMA loop.
 //  * Queries are read once per work item as bf16 and turned by RoPE through
 //    a (cos, sin) table into fp16 registers, so no rotated copy of Q is
 //    written.
@@ -30,7 +32,7 @@
 //    O += P V for tile j.
 //    sched_group_barrier interleaves the two instruction streams, so the
 //    softmax runs in the shadow of the MFMAs instead of after them.
-//  * Eight waves of 32 queries (256 queries per work-group) use ~240
+//  * Eight waves of 32 queries (256 queries per work-group) use 256
 //    VGPRs: one work-group per CU, two waves per SIMD, and one K/V tile DMA
 //    serves 256 queries.  In the last, partial query tile of a window, waves
 //    with no query left only take their share of the DMAs and barriers, so
@@ -43,8 +45,13 @@
 //    from -m, so the MFMA emits scores relative to the maximum and the
 //    softmax is one exp2 and half a packed conversion per score; the exp2
 //    go to the transcendental issue class, paired two per MFMA.
-//  * Work items are mapped XCD-aware: consecutive items (same head, same
-//    window) land on the same XCD and share its L2.
+//  * Persistent work-groups, one per CU, claim work items from per-XCD
+//    counters: consecutive items (same head, same window) run on the same
+//    XCD and share its L2, and the next item's first tile DMAs are issued
+//    before the current item's epilogue.
+//  * Queries, key tiles or value tiles outside fp16's comfortable range
+//    carry nonzero exponents; the items that meet one are listed by the
+//    plain kernel and run by a second kernel that undoes the scales in fp32.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
