@@ -225,6 +225,44 @@ def test_window_no_bridge_no_split_tiny(tiny):
     assert_close(to_host(out), o_ref, "window tiny no bridge/split")
 
 
+@pytest.fixture(scope="module")
+def one_head16():
+    """One head on a 16 x 16 grid: full and coarse attention are a single work
+    item and each window step has a handful, fewer than the 8 per-XCD shares
+    of the persistent attention kernel, so most work-groups find every share
+    empty and leave."""
+    wl = W.Workload("one-head-16", B=1, H=1, D=128, Gh=16, Gw=16, native_h=8, native_w=8, dtype="bf16",
+                    p1_steps=2, f_min=2, p2_steps=2, w_start=8, w_min=6, halo=1, bridge_k=4,
+                    latent_kind="half_columns")
+    q, k, v = W.make_qkv(wl, device="cpu", dtype="bf16")
+    return wl, q.cuda(), k.cuda(), v.cuda(), to_host(q), to_host(k), to_host(v)
+
+
+def test_fewer_items_than_xcd_shares(one_head16):
+    wl, q, k, v, qh, kh, vh = one_head16
+    p = A.problem_for(wl)
+    out = A.area_full_attn(p, q, k, v)
+    torch.cuda.synchronize()
+    assert_close(to_host(out), O.full_attention(qh, kh, vh, wl.Gh, wl.Gw, wl.rope_theta), "one head full (1 item)")
+    f = 2
+    kp, vp = A.area_pool_kv(p, f, k, v)
+    out = A.area_coarse_attn(p, f, q, kp, vp)
+    torch.cuda.synchronize()
+    kp_ref, vp_ref = O.pool_kv(kh, vh, wl.Gh, wl.Gw, f, A.POOL_MEAN, wl.rope_theta)
+    assert_close(to_host(out), O.coarse_attention(qh, kp_ref, vp_ref, wl.Gh, wl.Gw, f, wl.rope_theta),
+                 "one head coarse (1 item)")
+    lat = W.make_latent(wl)
+    _, Eq = A.area_dwt_detail(p, torch.from_numpy(lat).cuda())
+    Eq_ref = O.energy_fixed(O.detail_energy(lat))
+    for t in range(wl.p2_steps):
+        step = wl.p1_steps + t
+        plan, wsum, br, ref, br_ref = check_plan_step(wl, p, step, Eq, Eq_ref, k, kh)
+        out = A.area_window_attn(p, step, plan, wsum, br, q, k, v)
+        torch.cuda.synchronize()
+        o_ref = O.window_attention(qh, kh, vh, ref, br_ref, wl.Gh, wl.Gw, wl.rope_theta)
+        assert_close(to_host(out), o_ref, f"one head window step {t} ({len(ref.windows)} windows)")
+
+
 # ------------------------------------------------- flux-2048, full size ----
 
 @pytest.fixture(scope="module")
