@@ -432,7 +432,7 @@ def main():
     if not args.no_cpu_baseline:
         p, q, k, v, lat = m["tensors"]
         cpu = cpu_baseline(wl, q, k, v, lat, sc.sched, m["flops"], sc.win_pairs, sc.full_flops,
-                           coarse_rows=wl.N, rows=4096, full_rows=2048)
+                           coarse_rows=wl.N, rows=8192, full_rows=4096)
     headline = config_summary(wl, m, None)
 
     # ---- every other configured workload, measured in the same run
