@@ -218,6 +218,7 @@ struct BridgeWs {
 };
 
 // Keys saturate at this magnitude inside the mean-key sum only.
+
 constexpr float kMeanClamp = 268435456.0f;  // 2^28, exact in fp32
 
 BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
@@ -247,15 +248,24 @@ __global__ __launch_bounds__(256) void bridge_sum_kernel(const uint4* __restrict
   long long acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int r0 = chunk * kBridgeChunk, r1 = min(N, r0 + kBridgeChunk);
   const uint4* base = k + (bh * (int64_t)(T + N) + T) * CPR;  // the image rows of the sequence
-  for (int r = r0 + rr; r < r1; r += RPP) {
-    uint4 w = base[(int64_t)r * CPR + c];
-    const unsigned u[4] = {w.x, w.y, w.z, w.w};
+  // four rows in flight per thread; rows past the chunk read as zero keys
+  for (int r = r0 + rr; r < r1; r += 4 * RPP) {
+    uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double lo = (double)fminf(fmaxf(__uint_as_float(u[i] << 16), -kMeanClamp), kMeanClamp);
-      double hi = (double)fminf(fmaxf(__uint_as_float(u[i] & 0xFFFF0000u), -kMeanClamp), kMeanClamp);
-      acc[2 * i] += (long long)rint(lo * 16777216.0);
-      acc[2 * i + 1] += (long long)rint(hi * 16777216.0);
+    for (int j = 0; j < 4; ++j) {
+      const int rj = r + j * RPP;
+      w[j] = rj < r1 ? base[(int64_t)rj * CPR + c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double lo = (double)fminf(fmaxf(__uint_as_float(u[i] << 16), -kMeanClamp), kMeanClamp);
+        const double hi = (double)fminf(fmaxf(__uint_as_float(u[i] & 0xFFFF0000u), -kMeanClamp), kMeanClamp);
+        acc[2 * i] += (long long)rint(lo * 16777216.0);
+        acc[2 * i + 1] += (long long)rint(hi * 16777216.0);
+      }
     }
   }
 #pragma unroll
@@ -275,8 +285,18 @@ __global__ void bridge_mean_kernel(const long long* __restrict__ part, double* _
                                    int D) {
   int64_t bh = blockIdx.x;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    // eight independent partial sums keep eight chunk loads in flight
+    const long long* pd = part + (int64_t)bh * nch * D + d;
+    __int128 p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int c = 0;
+    for (; c + 8 <= nch; c += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] += pd[(int64_t)(c + j) * D];
+    }
+    for (; c < nch; ++c) p[0] += pd[(int64_t)c * D];
     __int128 s = 0;
-    for (int c = 0; c < nch; ++c) s += part[((int64_t)bh * nch + c) * D + d];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += p[j];
     const long long hi = (long long)(s >> 32);
     const unsigned lo = (unsigned)(s & 0xFFFFFFFF);
     mean[bh * D + d] = ((double)hi * 4294967296.0 + (double)lo) / (16777216.0 * (double)N);
