@@ -218,7 +218,6 @@ struct BridgeWs {
 };
 
 // Keys saturate at this magnitude inside the mean-key sum only.
-
 constexpr float kMeanClamp = 268435456.0f;  // 2^28, exact in fp32
 
 BridgeWs bridge_ws(void* ws, int64_t BH, int N, int D, int R) {
