@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   const int ky0 = rp[4], kx0 = rp[5], kw = rp[7];
   const int nrect = rp[6] * kw;
   const int cnt = R > 0 ? count[(int64_t)rec * BH + bh] : 0;
-  const int T = kv_tile_off[rec] + t;
+  const int gt = kv_tile_off[rec] + t;  // the tile's index among the gathered tiles
   if (threadIdx.x < BN) {
     int s = t * BN + threadIdx.x;
     int row = -1;  // sequence row of the slot's token
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   __syncthreads();
   const u16* ksrc = k + bh * (int64_t)(Tt + N) * D;
   const u16* vsrc = v + bh * (int64_t)(Tt + N) * D;
-  u16* kdst = kg + (bh * cap_tiles + T) * (int64_t)BN * D;
+  u16* kdst = kg + (bh * cap_tiles + gt) * (int64_t)BN * D;
   float kx[CH][8], vx[CH][8];
   float mk = 0.0f, mv = 0.0f;
 #pragma unroll
@@ -484,12 +484,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
     *reinterpret_cast<u32x4*>(buf + row * LS + col * 8) = f16x8_scaled(vx[i], ev);
   }
   if (threadIdx.x == 0) {
-    kexp[bh * cap_tiles + T] = ek;
-    vexp[bh * cap_tiles + T] = ev;
+    kexp[bh * cap_tiles + gt] = ek;
+    vexp[bh * cap_tiles + gt] = ev;
     if (ek | ev) flags[bh] = 1;
   }
   __syncthreads();
-  u16* vdst = vg + (bh * cap_tiles + T) * (int64_t)D * BN;
+  u16* vdst = vg + (bh * cap_tiles + gt) * (int64_t)D * BN;
   for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
     int d = c / (BN / 8), k8 = c - d * (BN / 8);
     u32x4 o;
