@@ -710,8 +710,10 @@ __device__ __attribute__((always_inline)) inline f16x8 lds_frag(const u16* stage
 // carry log2(e)/sqrt(D), and the first MFMA of each accumulator starts from
 // nm = -m instead of zero, so no per-score scale or subtraction is left.
 // With ZERO_START (the scaled loop) the accumulators start from zero and the
-// caller shifts and rescales the raw scores itself.
-template <int D, int QG, bool ZERO_START = false>
+// caller shifts and rescales the raw scores itself.  With LAST (an item's
+// last tile) no MFMA runs: only P and its sums, and phase B's first V^T
+// fragments are read.
+template <int D, int QG, bool ZERO_START = false, bool LAST = false>
 __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2], const u16* ks, int n, int hi,
                                                               const f16x8 (&qf)[QG][D / 16],
                                                               const f32x16 (&sc)[QG][2], const f32x16 (&nm)[QG],
@@ -730,16 +732,22 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
   for (int g = 0; g < QG; ++g) ps[g][0] = ps[g][1] = 0.0f;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const f16x8 f = fr[j % PF];
-    if (j + PF < NT) fr[j % PF] = lds_frag(ks, k_frag_off<D>(j + PF, n, hi));
-    else vfr[j + PF - NT] = lds_frag(vt, vt_frag_off<D>(j + PF - NT, n, hi));
+    if constexpr (LAST) {
+      if (j < PF) vfr[j] = lds_frag(vt, vt_frag_off<D>(j, n, hi));
+    } else {
+      const f16x8 f = fr[j % PF];
+      if (j + PF < NT) fr[j % PF] = lds_frag(ks, k_frag_off<D>(j + PF, n, hi));
+      else vfr[j + PF - NT] = lds_frag(vt, vt_frag_off<D>(j + PF - NT, n, hi));
 #pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if constexpr (ZERO_START) {
-        const f32x16 zero = {};
-        sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? zero : sn[g][j & 1], 0, 0, 0);
-      } else {
-        sn[g][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
+      for (int g = 0; g < QG; ++g) {
+        if constexpr (ZERO_START) {
+          const f32x16 zero = {};
+          sn[g][j & 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? zero : sn[g][j & 1], 0, 0, 0);
+        } else {
+          sn[g][j & 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(f, qf[g][j >> 1], j < 2 ? nm[g] : sn[g][j & 1], 0, 0, 0);
+        }
       }
     }
     // P of EPM scores, converted in pairs (one packed conversion per pair)
@@ -765,6 +773,7 @@ __device__ __attribute__((always_inline)) inline void phase_a(f32x16 (&sn)[QG][2
       }
   // issue order: per fragment its MFMAs, the next read (K, then V^T for
   // phase B), the exp2 of EPM scores and the conversion of the previous pair
+  if constexpr (LAST) return;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, QG, 0);
@@ -1011,24 +1020,29 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
   // next step.  A V^T tile stored at 2^-ev adds ev - ev_cur to its scores
   // (P carries 2^(ev - ev_cur)), and a tile with ev above ev_cur first moves
   // O to the new unit, so P never grows; l stays in true units.
-  auto step = [&](auto scaled_tag, f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn,
+  // The item's last step (last_tag) reads no K fragments, starts no DMA and
+  // computes no scores: phase A only turns the current scores into P.
+  auto step = [&](auto scaled_tag, auto last_tag, f32x16 (&scur)[QG][2], f32x16 (&snext)[QG][2], const u16* ksn,
                   const u16* vtc, int j, u16* kdma, int ktile, u16* vdma, int vtile)
       __attribute__((always_inline)) {
     constexpr bool SC = decltype(scaled_tag)::value;
-    // phase A's first K fragments, read ahead of the tile DMAs so their LDS
-    // latency overlaps them
+    constexpr bool LT = decltype(last_tag)::value;
     f16x8 kfr[kFragAhead];
+    if constexpr (!LT) {
+      // phase A's first K fragments, read ahead of the tile DMAs so their
+      // LDS latency overlaps them
 #pragma unroll
-    for (int jj = 0; jj < kFragAhead; ++jj)
-      kfr[jj] = lds_frag(ksn, k_frag_off<D>(jj, n, hi));
-    __builtin_amdgcn_sched_barrier(0);
-    // DMAs of the next tiles into the two free stages
-    issue_k<D>(kdma, ktile, tid, wave_u, nkv, kbase);
-    issue_v<D>(vdma, vtile, tid, wave_u, vtbase);
+      for (int jj = 0; jj < kFragAhead; ++jj)
+        kfr[jj] = lds_frag(ksn, k_frag_off<D>(jj, n, hi));
+      __builtin_amdgcn_sched_barrier(0);
+      // DMAs of the next tiles into the two free stages
+      issue_k<D>(kdma, ktile, tid, wave_u, nkv, kbase);
+      issue_v<D>(vdma, vtile, tid, wave_u, vtbase);
+    }
     f16x8 pf[QG][4];
     f16x8 vfr[kFragAhead];
     float psum[QG];
-    phase_a<D, QG, SC>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr, psum);
+    phase_a<D, QG, SC, LT>(snext, ksn, n, hi, qf, scur, nm, pf, kfr, vtc, vfr, psum);
     // keep P's computation in this block: its only use is after the branch
 #pragma unroll
     for (int g = 0; g < QG; ++g)
@@ -1081,7 +1095,9 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
       }
     }
     const int valid = nkv - (j + 1) * BN;
-    if (valid < BN) mask_tail<QG>(snext, valid, hi);
+    if constexpr (!LT) {
+      if (valid < BN) mask_tail<QG>(snext, valid, hi);
+    }
     phase_b<D, QG>(o, vtc, n, hi, pf, vfr);
     if constexpr (SC) {
 #pragma unroll
@@ -1120,10 +1136,9 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
 
   // Stage use: K tile t in ks[t % 2], V tile t in vt[t % 2].  Each step
   // reads its first K fragments, starts the DMAs into the two free stages,
-  // computes, then waits for its own DMAs and syncs.  No DMA is outstanding
-  // at a branch merge; the last half-iteration re-loads clamped tiles instead
-  // of branching around the DMA, and its scores of the tile past the end are
-  // never used.  The item's first three tile DMAs are already in flight.
+  // computes, then waits for its own DMAs and syncs; every step ends with
+  // one barrier, so an item takes nt of them.  No DMA is outstanding at a
+  // branch merge.  The item's first three tile DMAs are already in flight.
   f32x16 sa[QG][2], sb[QG][2];
   // Each query row carries its own power-of-two exponent eq (operand_exponent
   // of the row's largest turned and scaled magnitude, the two lanes of a
@@ -1211,36 +1226,51 @@ __device__ __attribute__((always_inline)) inline bool compute_item(
 #pragma unroll
   for (int g = 0; g < QG; ++g) any_q |= qs.qvalid[g];
   if (__any(any_q)) {
-    if constexpr (!scaled) {
-      for (int j = 0; j < nt; j += 2) {
-        step(std::false_type{}, sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
+    // Paired steps while at least three tiles remain, then one or two
+    // steps: the last one turns the last tile's scores into P and adds
+    // P V only, with no scores and no DMA past the end.  With two tiles
+    // left, the next-to-last step's scores move into sa first, so that one
+    // copy of the last step serves both parities; that step's K DMA
+    // reloads the last K tile (unused), as the idle waves' mirror does.
+    auto walk = [&](auto scaled_tag) __attribute__((always_inline)) {
+      int j = 0;
+      for (; j + 2 < nt; j += 2) {
+        step(scaled_tag, std::false_type{}, sa, sb, ks1, vt0, j, ks0, j + 2, vt1, j + 1);
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
-        if (j + 1 >= nt) break;
-        step(std::false_type{}, sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
-      }
-    } else {
-      for (int j = 0; j < nt; j += 2) {
-        step(std::true_type{}, sa, sb, ks1, vt0, j, ks0, min(j + 2, nt - 1), vt1, min(j + 1, nt - 1));
-        __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        __syncthreads();
-        if (j + 1 >= nt) break;
-        step(std::true_type{}, sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, min(j + 2, nt - 1));
+        step(scaled_tag, std::false_type{}, sb, sa, ks0, vt1, j + 1, ks1, min(j + 3, nt - 1), vt0, j + 2);
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
       }
-    }
+      const u16* vt_last = vt0;
+      if (j + 2 == nt) {
+        step(scaled_tag, std::false_type{}, sa, sb, ks1, vt0, j, ks0, j + 1, vt1, j + 1);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+          sa[g][0] = sb[g][0];
+          sa[g][1] = sb[g][1];
+        }
+        vt_last = vt1;
+        ++j;
+      }
+      step(scaled_tag, std::true_type{}, sa, sb, ks0, vt_last, j, ks1, 0, vt0, 0);
+      __syncthreads();
+    };
+    if constexpr (!scaled) walk(std::false_type{});
+    else walk(std::true_type{});
   } else {
     // none of this wave's queries is in the item (the last, partial query
     // tile of a window): it only takes its share of the same tile DMAs and
     // the same nt barriers as the computing waves
     for (int j = 0; j < nt; ++j) {
       const bool even = (j & 1) == 0;
-      issue_k<D>(even ? ks0 : ks1, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
-      issue_v<D>(even ? vt1 : vt0, min(j + 1, nt - 1), tid, wave_u, vtbase);
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      if (j + 1 < nt) {
+        issue_k<D>(even ? ks0 : ks1, min(j + 2, nt - 1), tid, wave_u, nkv, kbase);
+        issue_v<D>(even ? vt1 : vt0, j + 1, tid, wave_u, vtbase);
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      }
       __syncthreads();
     }
   }
