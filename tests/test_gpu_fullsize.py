@@ -175,6 +175,24 @@ def test_ragged_key_counts_dense(Gh, Gw):
     close(co.float().cpu().numpy(), O.coarse_attention(qh, kpr, vpr, Gh, Gw, 2, wl.rope_theta), f"coarse {Gh}x{Gw}")
 
 
+@pytest.mark.parametrize("Gh,Gw", [(4, 10), (8, 8), (8, 16), (10, 14), (12, 16), (10, 20), (16, 20), (20, 28)])
+def test_short_key_sets_one_to_three_tiles(Gh, Gw):
+    # key sets of 1, 2 and 3 64-key tiles, whole and ragged, through both orders of the item's last
+    # steps (full attention: N = 40 .. 560 keys, 1 to 9 tiles; coarse f = 2: 10 .. 140 pooled keys)
+    # (iid inputs: the smooth-noise generator's blur needs grids of 13 or more per side)
+    wl, p = small_problem(Gh, Gw, D=128, w_start=4, w_min=2, halo=1, bridge_k=2)
+    q, k, v = (torch.from_numpy(t).to(torch.bfloat16).cuda()
+               for t in W.random_small_qkv(wl.B, wl.H, Gh * Gw, wl.D, seed=8))
+    qh, kh, vh = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+    out = A.area_full_attn(p, q, k, v)
+    kp, vp = A.area_pool_kv(p, 2, k, v)
+    co = A.area_coarse_attn(p, 2, q, kp, vp)
+    torch.cuda.synchronize()
+    close(out.float().cpu().numpy(), O.full_attention(qh, kh, vh, Gh, Gw, wl.rope_theta), f"full {Gh}x{Gw}")
+    kpr, vpr = O.pool_kv(kh, vh, Gh, Gw, 2, O.POOL_MEAN, wl.rope_theta)
+    close(co.float().cpu().numpy(), O.coarse_attention(qh, kpr, vpr, Gh, Gw, 2, wl.rope_theta), f"coarse {Gh}x{Gw}")
+
+
 def test_batch_two_windowed():
     wl, p = small_problem(32, 48, H=3, B=2, D=128, w_start=20, w_min=12, halo=2, bridge_k=12)
     q, k, v = (t.cuda() for t in W.make_qkv(wl, device="cpu", dtype="bf16", seed=6))
