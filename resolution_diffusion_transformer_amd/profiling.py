@@ -2,12 +2,15 @@
 
     python -m resolution_diffusion_transformer_amd.profiling stats <kernel_stats.csv>
     python -m resolution_diffusion_transformer_amd.profiling counters <counter_collection.csv> [COUNTER]
+    python -m resolution_diffusion_transformer_amd.profiling dispatches <kernel_trace.csv> NAME [NAME ...]
 
 `stats` prints the per-kernel call count and average/total duration from
 `rocprofv3 --kernel-trace --stats --output-format csv`.  `counters` prints,
 per kernel, the dispatch count and the per-dispatch average of each counter
 from `rocprofv3 --pmc ... --output-format csv` (counters reported per
-hardware instance are summed within a dispatch first).
+hardware instance are summed within a dispatch first).  `dispatches` prints,
+for each kernel whose name contains one of the NAMEs, the duration of every
+dispatch in launch order (from `rocprofv3 --kernel-trace --output-format csv`).
 """
 from __future__ import annotations
 
@@ -69,12 +72,34 @@ def format_counters(cs, only=None) -> str:
     return "\n".join(lines)
 
 
+def dispatches(path: str, names):
+    """{kernel: [duration ns of each dispatch, in launch order]} for kernels
+    whose name contains one of `names`."""
+    rows = [r for r in csv.DictReader(open(path)) if any(n in r["Kernel_Name"] for n in names)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    out = collections.defaultdict(list)
+    for r in rows:
+        out[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def format_dispatches(ds) -> str:
+    lines = []
+    for k, durs in ds.items():
+        lines.append(f"{short_name(k)}: {len(durs)} dispatches, us:")
+        for i in range(0, len(durs), 10):
+            lines.append("  " + " ".join(f"{d / 1e3:8.1f}" for d in durs[i:i + 10]))
+    return "\n".join(lines)
+
+
 def main(argv):
-    if len(argv) < 2 or argv[0] not in ("stats", "counters"):
+    if len(argv) < 2 or argv[0] not in ("stats", "counters", "dispatches"):
         print(__doc__)
         return 2
     if argv[0] == "stats":
         print(format_stats(kernel_stats(argv[1])))
+    elif argv[0] == "dispatches":
+        print(format_dispatches(dispatches(argv[1], argv[2:])))
     else:
         print(format_counters(counters(argv[1]), argv[2] if len(argv) > 2 else None))
     return 0

@@ -69,3 +69,19 @@ def test_bench_traffic_counts_only_for_the_profiled_source(tmp_path, monkeypatch
     assert bench.measured_traffic("other") is None
     src.write_bytes(b"// kernel source, edited\n")
     assert bench.measured_traffic("demo") is None
+
+
+def test_dispatches_in_launch_order_per_kernel(tmp_path):
+    path = tmp_path / "t.csv"
+    _write_csv(path, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], [
+        ["blend_kernel(BlendArgs)", 300, 350],
+        ["gather_kernel<128>()", 100, 1100],
+        ["blend_kernel(BlendArgs)", 50, 80],
+        ["attn_kernel<128, true>()", 0, 10],
+    ])
+    ds = P.dispatches(str(path), ["blend_kernel", "gather_kernel"])
+    assert ds["blend_kernel(BlendArgs)"] == [30, 50]
+    assert ds["gather_kernel<128>()"] == [1000]
+    assert "attn_kernel<128, true>()" not in ds
+    text = P.format_dispatches(ds)
+    assert "blend_kernel(BlendArgs): 2 dispatches" in text and "0.0" in text
